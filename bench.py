@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Throughput of the chunked causal attention hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic
+inputs already resident in HBM.  For a worker-share workload (default: the
+grouped-query 64/8-head, head_dim 128 case at a 32768-token chunk, worker
+15 of 16 on a 524288-token sequence) the step is that worker's share of the
+load-balanced schedule:
+    its 9 forward pairs (1 diagonal + 8 full),
+    the LSE merge of all 16 partials of its query chunk (the 7 computed by
+    helpers are inputs, prepared before timing, as received messages),
+    the backward of its 9 pairs from the merged O and LSE (delta once),
+including zeroing the fp32 gradient accumulators.  Whole-sequence workloads
+run every pair, every merge and (if any) every backward.
+
+Prints ONE JSON line.  TFLOP/s counts only unmasked (query, key) pairs:
+forward 4*d and backward 10*d FLOP per pair per query head.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "causal attn fwd+bwd TFLOP/s (1 GPU) at 32K chunk; % of bf16 MFMA peak"
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # MI355X dense MFMA peaks
+
+
+def pairs_of(kind: int, c: int) -> int:
+    return c * (c + 1) // 2 if kind == 0 else c * c
+
+
+def gen_inputs(w, chunks_q, chunks_kv, backward):
+    """Seeded per-chunk inputs (numpy float32, bf16-exact), drawn in threads."""
+    import concurrent.futures as cf
+
+    from long_context_exact_amd.synth import TENSOR_DO, TENSOR_K, TENSOR_Q, TENSOR_V
+
+    jobs = [(TENSOR_Q, a) for a in chunks_q] + [(TENSOR_K, c) for c in chunks_kv] + \
+           [(TENSOR_V, c) for c in chunks_kv] + ([(TENSOR_DO, a) for a in chunks_q] if backward else [])
+    with cf.ThreadPoolExecutor(min(16, os.cpu_count() or 4)) as ex:
+        arrs = list(ex.map(lambda j: w.chunk_input(*j), jobs))
+    out = {0: {}, 1: {}, 2: {}, 3: {}}
+    for (tid, c), x in zip(jobs, arrs):
+        out[tid][c] = x
+    return out
+
+
+def cpu_baseline(w, host, worker, budget_s):
+    """The float64 oracle, as it stands, on a bounded sample of the same
+    workload: the last R query rows of the measured query chunk, query head 0,
+    over their whole causal prefix, forward + backward."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+
+    a = worker if worker >= 0 else w.workers - 1
+    c = w.chunk
+    kpre = np.concatenate([host[1][j][:, :, :1] for j in range(a + 1)], axis=1).astype(np.float64)
+    vpre = np.concatenate([host[2][j][:, :, :1] for j in range(a + 1)], axis=1).astype(np.float64)
+
+    def run(r):
+        q = host[0][a][:, c - r:, :1].astype(np.float64)
+        do = host[3][a][:, c - r:, :1].astype(np.float64) if 3 in host and a in host[3] else \
+            np.ones_like(q)
+        q0 = a * c + c - r
+        t0 = time.perf_counter()
+        o, lse = oracle.attention_fwd(q, kpre, vpre, w.scale, True, q0, 0)
+        oracle.attention_bwd(q, kpre, vpre, o, lse, do, w.scale, True, q0, 0)
+        dt = time.perf_counter() - t0
+        pairs = sum(q0 + i + 1 for i in range(r))
+        return dt, pairs * 14 * w.head_dim
+
+    r = 8
+    dt, _ = run(r)
+    r = int(max(8, min(c, r * budget_s / max(dt, 1e-3))))
+    dt, flops = run(r)
+    threads = sum(i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas")
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads or 1),
+            "kind": "oracle",
+            "sample": f"float64 numpy oracle, fwd+bwd of the last {r} query rows of chunk {a}, "
+                      f"query head 0, over their full causal prefix ({a * c + c} keys); "
+                      f"{dt:.1f} s, {flops:.3e} algorithmic FLOP"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="gqa64x8_512k_w15")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the schedule's "
+              "workers are emulated as work items on one device); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from long_context_exact_amd import dfa
+    from long_context_exact_amd.runner import ChunkedCausalAttention
+    from long_context_exact_amd.synth import WORKLOADS
+
+    w = WORKLOADS[args.workload]
+    dev = "cuda"
+    td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    att = ChunkedCausalAttention(w.workers, w.chunk, w.batch, w.heads_q, w.heads_kv, w.head_dim,
+                                 w.dtype, True)
+    if w.share_of >= 0:
+        owners = [w.share_of]
+        timed = att.items_of_worker(w.share_of)
+        assert all(it[5] == w.share_of for it in timed)
+        merged = {w.share_of: att.items_of_owner(w.share_of)}
+    else:
+        owners = list(range(w.workers))
+        timed = att.items
+        merged = {a: att.items_of_owner(a) for a in owners}
+    kv_needed = sorted({it[3] for its in merged.values() for it in its})
+
+    t0 = time.perf_counter()
+    host = gen_inputs(w, owners, kv_needed, w.backward)
+    q = {a: torch.from_numpy(host[0][a]).to(dev).to(td) for a in owners}
+    k = {c: torch.from_numpy(host[1][c]).to(dev).to(td) for c in kv_needed}
+    v = {c: torch.from_numpy(host[2][c]).to(dev).to(td) for c in kv_needed}
+    d_o = {a: torch.from_numpy(host[3][a]).to(dev).to(td) for a in owners} if w.backward else {}
+    gen_s = time.perf_counter() - t0
+
+    partials = {(it[2], it[3]): att.new_partial(dev) for its in merged.values() for it in its}
+    helpers = [it for its in merged.values() for it in its if it not in timed]
+    att.forward_items(helpers, q, k, v, partials)          # received messages: untimed
+    o = {a: torch.empty(att.q_shape(), dtype=td, device=dev) for a in owners}
+    lse = {a: torch.empty(att.lse_shape(), device=dev) for a in owners}
+    delta = {a: torch.empty(att.lse_shape(), device=dev) for a in owners}
+    dq = {a: torch.zeros(att.q_shape(), device=dev) for a in owners}
+    own_kv = sorted({it[3] for it in timed})
+    dk = {c: torch.zeros(att.kv_shape(), device=dev) for c in own_kv}
+    dv = {c: torch.zeros(att.kv_shape(), device=dev) for c in own_kv}
+
+    def step():
+        if w.backward:
+            for a in owners:
+                dq[a].zero_()
+            for c in own_kv:
+                dk[c].zero_()
+                dv[c].zero_()
+        att.forward_items(timed, q, k, v, partials)
+        for a in owners:
+            att.merge_owner(a, partials, o[a], lse[a])
+        if w.backward:
+            att.backward_items(timed, q, k, v, o, lse, d_o, delta, dq, dk, dv)
+
+    per_pair = w.batch * w.heads_q * w.head_dim
+    fwd_flop = sum(pairs_of(it[4], w.chunk) for it in timed) * per_pair * 4
+    bwd_flop = sum(pairs_of(it[4], w.chunk) for it in timed) * per_pair * 10 if w.backward else 0
+    flop = fwd_flop + bwd_flop
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    tflops = flop / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+
+    # Per-launch timing of the two compute calls (HIP events on the stream the
+    # library launches on: torch's current stream).
+    stream = torch.cuda.current_stream()
+
+    def per_call(fn, items):
+        evs = []
+        for it in items:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn(it)
+            e1.record(stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs)
+
+    fwd_ms = per_call(lambda it: dfa.dfa_attn_fwd_partial(att.desc(it[2], it[3]), q[it[2]],
+                                                          k[it[3]], v[it[3]],
+                                                          *partials[(it[2], it[3])]), timed)
+    kernels = {"fwd_bf16_kernel": (fwd_ms, fwd_flop, len(timed))}
+    if w.backward:
+        bwd_ms = per_call(lambda it: dfa.dfa_attn_bwd(att.desc(it[2], it[3]), q[it[2]], k[it[3]],
+                                                      v[it[3]], None, lse[it[2]], d_o[it[2]],
+                                                      delta[it[2]], False, dq[it[2]], dk[it[3]],
+                                                      dv[it[3]]), timed)
+        kernels["dkdv_bf16_kernel+dq_bf16_kernel"] = (bwd_ms, bwd_flop, len(timed))
+    name, (kms, kflop, nl) = max(kernels.items(), key=lambda kv: kv[1][0])
+    achieved = kflop / (kms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": name, "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                "avg_launch_ms": round(kms / nl, 4), "launches_per_step": nl,
+                "algorithmic_flop_per_launch": kflop / nl,
+                "others": {n: {"ms_per_step": round(x[0], 3),
+                               "tflops": round(x[1] / (x[0] * 1e-3) / 1e12, 2)}
+                           for n, x in kernels.items()}}
+
+    result = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "pct_of_peak": round(100 * tflops / peak, 2),
+        "config": {"workload": w.name, "chunk": w.chunk, "workers": w.workers,
+                   "total_seq": w.total_len, "heads_q": w.heads_q, "heads_kv": w.heads_kv,
+                   "head_dim": w.head_dim, "batch": w.batch,
+                   "share": (f"worker {w.share_of} of {w.workers}" if w.share_of >= 0
+                             else "all pairs"),
+                   "pairs_timed": len(timed), "backward": w.backward,
+                   "algorithmic_flop_per_step": flop, "wall_s_timed": round(wall, 3),
+                   "input_gen_s": round(gen_s, 1)},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        del q, k, v, d_o, partials, o, lse, delta, dq, dk, dv
+        torch.cuda.empty_cache()
+        result["cpu_baseline"] = cpu_baseline(w, host, w.share_of, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,172 @@
+/*
+ * dfa.h — C ABI of libdfa.so, the MI355X (gfx950) hot path of DistFlashAttn:
+ * blockwise exact causal softmax attention over token chunks.
+ *
+ * Source of the operations: "DISTFLASHATTN: Distributed Memory-efficient
+ * Attention for Long-context LLMs Training" (arXiv 2310.03294), as
+ * summarised section by section on its paperlayer.ai page.  The paper
+ * prints no API; every call below restates one operation that the paper
+ * describes, cited by its section / figure / appendix.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Layouts (row-major, head_dim contiguous):
+ *   Q, O, dO, dQ, O_partial : [batch, len_q,  heads_q,  head_dim]
+ *   K, V, dK, dV            : [batch, len_kv, heads_kv, head_dim]
+ *   LSE, delta              : [batch, heads_q, len_q]            (float32)
+ * Query head h reads key/value head h / (heads_q / heads_kv) (contiguous
+ * grouped-query groups).  LSE is the natural-log log-sum-exp of the scaled
+ * scores of a row; a row that sees no key has O = 0 and LSE = -inf.
+ *
+ * Memory: every tensor pointer is DEVICE memory owned by the caller; the
+ * library never allocates, frees or retains it.  Descriptors, work-item
+ * arrays and the pointer arrays of dfa_lse_merge are HOST memory read
+ * during the call only.
+ *
+ * Asynchrony: work is enqueued on `hip_stream` (a hipStream_t; NULL = the
+ * null stream) and the call returns after enqueueing.  Nothing synchronises.
+ *
+ * Errors: arguments are checked before anything is enqueued; on a non-OK
+ * status nothing was enqueued (except DFA_ERR_HIP, where a launch failed)
+ * and dfa_last_error() holds a message.  No C++ exception crosses the ABI.
+ * dfa_balanced_schedule and all argument checks never touch the HIP
+ * runtime, so they work on a machine without a GPU.
+ *
+ * Thread safety: every call is stateless and may be made from any thread.
+ */
+#ifndef DFA_H
+#define DFA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DFA_OK = 0,
+  DFA_ERR_INVALID = 1,      /* malformed argument (null pointer, bad shape) */
+  DFA_ERR_UNSUPPORTED = 2,  /* well-formed but not implemented (head_dim)   */
+  DFA_ERR_CAPACITY = 3,     /* output array too small; required size given  */
+  DFA_ERR_HIP = 4           /* the HIP runtime reported an error            */
+} dfa_status;
+
+typedef enum { DFA_F32 = 0, DFA_BF16 = 1 } dfa_dtype;
+
+/* One chunk pair of a schedule.  kind: 0 = diagonal pair (q_chunk ==
+ * kv_chunk, needs the causal element mask), 1 = full pair (q_chunk >
+ * kv_chunk, every score visible).  owner = q_chunk: the worker whose query
+ * rows these are; owner != worker marks a helper item. */
+typedef struct {
+  int32_t step, worker, q_chunk, kv_chunk, kind, owner;
+} dfa_work_item;
+
+/* Shape and masking of one (query chunk, key/value chunk) pair. */
+typedef struct {
+  int32_t batch;        /* >= 1                                            */
+  int32_t heads_q;      /* >= 1, a multiple of heads_kv                    */
+  int32_t heads_kv;     /* >= 1                                            */
+  int32_t head_dim;     /* 64 or 128 (else DFA_ERR_UNSUPPORTED)            */
+  int64_t len_q;        /* query rows in the chunk, >= 0, any value        */
+  int64_t len_kv;       /* key rows in the chunk,   >= 0, any value        */
+  int64_t q_start;      /* global token index of query row 0,  >= 0        */
+  int64_t kv_start;     /* global token index of key row 0,    >= 0        */
+  int32_t causal;       /* 1: key j visible to query i iff
+                               kv_start + j <= q_start + i; 0: all visible */
+  float scale;          /* score scale sigma (1/sqrt(head_dim)), finite    */
+  dfa_dtype dtype;      /* element type of Q, K, V, O (final) and dO       */
+} dfa_attn_desc;
+
+/* Chunk-pair schedule of P = num_workers workers over P contiguous chunks
+ * ([DistFlashAttn §3.2 and Fig. 3; App. B, Figs. 5-6]).
+ *   balanced = 0: unbalanced causal ring — at step t worker w >= t does
+ *     (w, w - t), the others idle; P steps.
+ *   balanced = 1: token-level load balancing — step 0 every worker does
+ *     its diagonal; at step t = 1..P/2 worker w >= t does (w, w - t) and a
+ *     worker h < t helps owner h + P - t with (h + P - t, h) using its own
+ *     key/value chunk, unless P - t == t; 1 + floor(P/2) steps.
+ * Writes the P(P+1)/2 items, sorted by (step, worker), to the HOST array
+ * `items` of `capacity` entries; *num_items and *num_steps receive the
+ * counts.  If capacity is too small: DFA_ERR_CAPACITY with *num_items set
+ * to the required count and nothing written.  `items` may be NULL when
+ * capacity == 0 (a size query).  num_workers must be in [1, 65536]. */
+dfa_status dfa_balanced_schedule(int32_t num_workers, int32_t balanced,
+                                 dfa_work_item* items, int64_t capacity,
+                                 int64_t* num_items, int32_t* num_steps);
+
+/* Partial attention of one chunk pair: the normalised output and its LSE
+ * ([DistFlashAttn App. D]: the forward returns output and logsumexp values;
+ * §3.2: partial outputs and softmax statistics are what a helper returns).
+ *   q [B,len_q,Hq,d], k and v [B,len_kv,Hkv,d] in desc->dtype;
+ *   o_part [B,len_q,Hq,d] float32 and lse [B,Hq,len_q] float32 are
+ *   overwritten.  Only the causal prefix is computed: key tiles entirely
+ *   after a query tile's last row are skipped (§2, §3.2). */
+dfa_status dfa_attn_fwd_partial(const dfa_attn_desc* desc, const void* q,
+                                const void* k, const void* v, float* o_part,
+                                float* lse, void* hip_stream);
+
+/* LSE merge of n partial states of the same query rows over disjoint key
+ * sets ([DistFlashAttn §3.2, Fig. 3]: the owner rescales the partials it
+ * receives with their softmax statistics):
+ *   M = max_r LSE_r;  LSE = M + ln sum_r exp(LSE_r - M);
+ *   O = sum_r exp(LSE_r - LSE) * O_r,   in ascending r, float32 math;
+ *   rows with every LSE_r = -inf give O = 0, LSE = -inf.
+ * o_parts / lse_parts: HOST arrays of n DEVICE pointers to float32
+ * [batch,len_q,heads,head_dim] / [batch,heads,len_q].  o_out is written in
+ * out_dtype, lse_out in float32.  o_out may alias o_parts[0] only when
+ * out_dtype == DFA_F32 (each element is read before it is written);
+ * lse_out may alias lse_parts[0].  1 <= n <= 64. */
+dfa_status dfa_lse_merge(int32_t n, const float* const* o_parts,
+                         const float* const* lse_parts, int32_t batch,
+                         int32_t heads, int64_t len_q, int32_t head_dim,
+                         dfa_dtype out_dtype, void* o_out, float* lse_out,
+                         void* hip_stream);
+
+/* Backward of one chunk pair from the SAVED final output and LSE; the
+ * forward is never recomputed ([DistFlashAttn §3.3]: checkpointing the
+ * FlashAttention output lets its backward reuse it, so the forward runs
+ * once).  With P = exp(sigma*QK^T - LSE) on the visible scores:
+ *   delta = rowsum(dO * O)                   (computed iff compute_delta)
+ *   dS    = P * (dO V^T - delta)
+ *   dq   += sigma * dS K        [B,len_q, Hq, d]  float32
+ *   dk   += sigma * dS^T Q      [B,len_kv,Hkv,d]  float32, summed over the
+ *   dv   += P^T dO              [B,len_kv,Hkv,d]  float32  query-head group
+ * o and d_o are [B,len_q,Hq,d] in desc->dtype; lse is the final (merged)
+ * [B,Hq,len_q].  delta [B,Hq,len_q] float32 is written when compute_delta
+ * is 1 and read otherwise (pass 1 on the first pair of a query chunk and 0
+ * on its other pairs).  dq, dk, dv accumulate (+=): the caller zeroes them
+ * once and sums over pairs (App. D: the backward returns gradient partials
+ * to their owners).  Each call is deterministic. */
+dfa_status dfa_attn_bwd(const dfa_attn_desc* desc, const void* q,
+                        const void* k, const void* v, const void* o,
+                        const float* lse, const void* d_o, float* delta,
+                        int32_t compute_delta, float* dq, float* dk,
+                        float* dv, void* hip_stream);
+
+/* Message of the last non-OK status on the calling thread ("" if none). */
+const char* dfa_last_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int32_t dfa_version(void);
+
+/* ---- test support: not part of the hot path ---------------------------
+ * Tile shape (query rows per workgroup tile, keys per key tile) that
+ * dfa_attn_fwd_partial uses for this descriptor. */
+dfa_status dfa_test_tile_shape(const dfa_attn_desc* desc, int32_t* bm,
+                               int32_t* bn);
+
+/* Runs the same forward as dfa_attn_fwd_partial and records, per batch
+ * row 0 and query-head tile 0, which (query tile, key tile) pairs the
+ * kernel visited: visits [ceil(len_q/bm), ceil(len_kv/bn)] uint8 DEVICE
+ * array, caller-zeroed; 1 = visited without the causal element mask,
+ * 2 = visited with it, 0 = skipped. */
+dfa_status dfa_test_fwd_tile_visits(const dfa_attn_desc* desc, const void* q,
+                                    const void* k, const void* v,
+                                    float* o_part, float* lse,
+                                    uint8_t* visits, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFA_H */

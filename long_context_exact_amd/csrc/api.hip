@@ -1,0 +1,187 @@
+// C ABI entry points of libdfa: argument checks (no HIP call before they
+// pass), then dispatch to the kernels on the caller's stream.
+#include <cstring>
+#include <string>
+
+#include "kernels.hpp"
+
+namespace dfa {
+
+dfa_status check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(DFA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return DFA_OK;
+}
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks shared by every call that takes a descriptor.
+dfa_status check_desc(const char* fn, const dfa_attn_desc* d) {
+  const std::string f(fn);
+  if (d == nullptr) return fail(DFA_ERR_INVALID, f + ": desc is null");
+  if (d->batch < 0 || d->batch > 65535)
+    return fail(DFA_ERR_INVALID, f + ": batch must be in [0, 65535]");
+  if (d->heads_q < 1 || d->heads_kv < 1 || d->heads_q % d->heads_kv != 0)
+    return fail(DFA_ERR_INVALID, f + ": heads_q must be a positive multiple of heads_kv >= 1");
+  if (d->len_q < 0 || d->len_kv < 0 || d->q_start < 0 || d->kv_start < 0)
+    return fail(DFA_ERR_INVALID, f + ": lengths and starts must be >= 0");
+  if (d->causal != 0 && d->causal != 1) return fail(DFA_ERR_INVALID, f + ": causal must be 0 or 1");
+  if (!std::isfinite(d->scale) || d->scale < 0.f)
+    return fail(DFA_ERR_INVALID, f + ": scale must be finite and >= 0");
+  if (d->dtype != DFA_F32 && d->dtype != DFA_BF16)
+    return fail(DFA_ERR_INVALID, f + ": unknown dtype");
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(DFA_ERR_UNSUPPORTED,
+                f + ": head_dim " + std::to_string(d->head_dim) + " unsupported (64 or 128)");
+  // grid extents: query tiles x head groups must fit a 32-bit grid
+  if (d->len_q > (int64_t(1) << 40) || d->len_kv > (int64_t(1) << 40))
+    return fail(DFA_ERR_INVALID, f + ": chunk length too large");
+  if (cdiv(d->len_q, 4) * d->heads_q > INT32_MAX || cdiv(d->len_kv, 4) * d->heads_kv > INT32_MAX)
+    return fail(DFA_ERR_INVALID, f + ": problem exceeds the launch grid");
+  return DFA_OK;
+}
+
+dfa_status need(const std::string& fn, const void* p, const char* name, bool vec) {
+  if (p == nullptr) return fail(DFA_ERR_INVALID, fn + ": " + name + " is null");
+  if (vec && !aligned16(p))
+    return fail(DFA_ERR_INVALID, fn + ": " + name + " must be 16-byte aligned");
+  return DFA_OK;
+}
+
+#define DFA_TRY(expr)                    \
+  do {                                   \
+    const dfa_status _st = (expr);       \
+    if (_st != DFA_OK) return _st;       \
+  } while (0)
+
+dfa_status fwd_common(const char* fn, const dfa_attn_desc* desc, const void* q, const void* k,
+                      const void* v, float* o_part, float* lse, uint8_t* visits,
+                      void* hip_stream) {
+  DFA_TRY(check_desc(fn, desc));
+  const dfa_attn_desc& d = *desc;
+  const std::string f(fn);
+  if (d.batch == 0 || d.len_q == 0) return DFA_OK;
+  DFA_TRY(need(f, q, "q", true));
+  DFA_TRY(need(f, o_part, "o_part", true));
+  DFA_TRY(need(f, lse, "lse", false));
+  const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (d.len_kv == 0) {
+    if (visits != nullptr) return DFA_OK;  // no key tiles: nothing visited
+    return launch_fill_empty(int64_t(d.batch) * d.len_q * d.heads_q * d.head_dim, o_part,
+                             int64_t(d.batch) * d.heads_q * d.len_q, lse, s);
+  }
+  DFA_TRY(need(f, k, "k", true));
+  DFA_TRY(need(f, v, "v", true));
+  return launch_fwd(d, q, k, v, o_part, lse, visits, s);
+}
+
+}  // namespace
+}  // namespace dfa
+
+using namespace dfa;
+
+extern "C" dfa_status dfa_attn_fwd_partial(const dfa_attn_desc* desc, const void* q,
+                                           const void* k, const void* v, float* o_part,
+                                           float* lse, void* hip_stream) {
+  try {
+    return fwd_common("dfa_attn_fwd_partial", desc, q, k, v, o_part, lse, nullptr, hip_stream);
+  } catch (...) {
+    return fail(DFA_ERR_INVALID, "dfa_attn_fwd_partial: internal error");
+  }
+}
+
+extern "C" dfa_status dfa_lse_merge(int32_t n, const float* const* o_parts,
+                                    const float* const* lse_parts, int32_t batch, int32_t heads,
+                                    int64_t len_q, int32_t head_dim, dfa_dtype out_dtype,
+                                    void* o_out, float* lse_out, void* hip_stream) {
+  try {
+    const std::string f("dfa_lse_merge");
+    if (n < 1 || n > 64) return fail(DFA_ERR_INVALID, f + ": n must be in [1, 64]");
+    if (o_parts == nullptr || lse_parts == nullptr)
+      return fail(DFA_ERR_INVALID, f + ": o_parts / lse_parts arrays are null");
+    if (batch < 0 || heads < 1 || len_q < 0)
+      return fail(DFA_ERR_INVALID, f + ": batch >= 0, heads >= 1, len_q >= 0 required");
+    if (out_dtype != DFA_F32 && out_dtype != DFA_BF16)
+      return fail(DFA_ERR_INVALID, f + ": unknown out_dtype");
+    if (head_dim != 64 && head_dim != 128)
+      return fail(DFA_ERR_UNSUPPORTED, f + ": head_dim must be 64 or 128");
+    if (int64_t(batch) * len_q * heads * (head_dim / 4) > (int64_t(INT32_MAX) * 256))
+      return fail(DFA_ERR_INVALID, f + ": problem exceeds the launch grid");
+    if (batch == 0 || len_q == 0) return DFA_OK;
+    for (int r = 0; r < n; ++r) {
+      DFA_TRY(need(f, o_parts[r], "o_parts[r]", true));
+      DFA_TRY(need(f, lse_parts[r], "lse_parts[r]", false));
+      if (static_cast<const void*>(o_parts[r]) == o_out && (r > 0 || out_dtype != DFA_F32))
+        return fail(DFA_ERR_INVALID,
+                    f + ": o_out may alias only o_parts[0], and only with DFA_F32 output");
+      if (r > 0 && lse_parts[r] == lse_out)
+        return fail(DFA_ERR_INVALID, f + ": lse_out may alias only lse_parts[0]");
+    }
+    DFA_TRY(need(f, o_out, "o_out", out_dtype == DFA_F32));
+    if (out_dtype == DFA_BF16 && (reinterpret_cast<uintptr_t>(o_out) & 7u))
+      return fail(DFA_ERR_INVALID, f + ": o_out must be 8-byte aligned");
+    DFA_TRY(need(f, lse_out, "lse_out", false));
+    return launch_merge(n, o_parts, lse_parts, batch, heads, len_q, head_dim, out_dtype, o_out,
+                        lse_out, static_cast<hipStream_t>(hip_stream));
+  } catch (...) {
+    return fail(DFA_ERR_INVALID, "dfa_lse_merge: internal error");
+  }
+}
+
+extern "C" dfa_status dfa_attn_bwd(const dfa_attn_desc* desc, const void* q, const void* k,
+                                   const void* v, const void* o, const float* lse,
+                                   const void* d_o, float* delta, int32_t compute_delta,
+                                   float* dq, float* dk, float* dv, void* hip_stream) {
+  try {
+    const char* fn = "dfa_attn_bwd";
+    const std::string f(fn);
+    DFA_TRY(check_desc(fn, desc));
+    const dfa_attn_desc& d = *desc;
+    if (compute_delta != 0 && compute_delta != 1)
+      return fail(DFA_ERR_INVALID, f + ": compute_delta must be 0 or 1");
+    if (d.batch == 0 || d.len_q == 0 || d.len_kv == 0) return DFA_OK;  // nothing to add
+    DFA_TRY(need(f, q, "q", true));
+    DFA_TRY(need(f, k, "k", true));
+    DFA_TRY(need(f, v, "v", true));
+    DFA_TRY(need(f, d_o, "d_o", true));
+    DFA_TRY(need(f, lse, "lse", false));
+    DFA_TRY(need(f, delta, "delta", false));
+    DFA_TRY(need(f, dq, "dq", true));
+    DFA_TRY(need(f, dk, "dk", true));
+    DFA_TRY(need(f, dv, "dv", true));
+    if (compute_delta) DFA_TRY(need(f, o, "o", true));
+    const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    if (compute_delta) DFA_TRY(launch_delta(d, o, d_o, delta, s));
+    return launch_bwd(d, q, k, v, lse, d_o, delta, dq, dk, dv, s);
+  } catch (...) {
+    return fail(DFA_ERR_INVALID, "dfa_attn_bwd: internal error");
+  }
+}
+
+extern "C" int32_t dfa_version(void) { return 100; }
+
+extern "C" dfa_status dfa_test_tile_shape(const dfa_attn_desc* desc, int32_t* bm, int32_t* bn) {
+  DFA_TRY(check_desc("dfa_test_tile_shape", desc));
+  if (bm == nullptr || bn == nullptr)
+    return fail(DFA_ERR_INVALID, "dfa_test_tile_shape: bm / bn are null");
+  fwd_tile_shape(*desc, bm, bn);
+  return DFA_OK;
+}
+
+extern "C" dfa_status dfa_test_fwd_tile_visits(const dfa_attn_desc* desc, const void* q,
+                                               const void* k, const void* v, float* o_part,
+                                               float* lse, uint8_t* visits, void* hip_stream) {
+  try {
+    DFA_TRY(check_desc("dfa_test_fwd_tile_visits", desc));
+    if (desc->dtype != DFA_BF16)
+      return fail(DFA_ERR_UNSUPPORTED, "dfa_test_fwd_tile_visits: bf16 (tiled) path only");
+    if (visits == nullptr) return fail(DFA_ERR_INVALID, "dfa_test_fwd_tile_visits: visits is null");
+    return fwd_common("dfa_test_fwd_tile_visits", desc, q, k, v, o_part, lse, visits,
+                      hip_stream);
+  } catch (...) {
+    return fail(DFA_ERR_INVALID, "dfa_test_fwd_tile_visits: internal error");
+  }
+}

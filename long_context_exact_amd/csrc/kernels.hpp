@@ -1,0 +1,33 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include "common.hpp"
+
+namespace dfa {
+
+// Forward of one chunk pair (bf16 -> MFMA kernel, f32 -> exact fp32 kernel).
+// visits: optional tile-visit record (test support), else nullptr.
+dfa_status launch_fwd(const dfa_attn_desc& d, const void* q, const void* k,
+                      const void* v, float* o, float* lse, uint8_t* visits,
+                      hipStream_t s);
+void fwd_tile_shape(const dfa_attn_desc& d, int32_t* bm, int32_t* bn);
+
+dfa_status launch_merge(int32_t n, const float* const* o_parts,
+                        const float* const* lse_parts, int32_t batch,
+                        int32_t heads, int64_t len_q, int32_t head_dim,
+                        dfa_dtype out_dtype, void* o_out, float* lse_out,
+                        hipStream_t s);
+
+dfa_status launch_delta(const dfa_attn_desc& d, const void* o, const void* d_o,
+                        float* delta, hipStream_t s);
+
+dfa_status launch_bwd(const dfa_attn_desc& d, const void* q, const void* k,
+                      const void* v, const float* lse, const void* d_o,
+                      const float* delta, float* dq, float* dk, float* dv,
+                      hipStream_t s);
+
+// o = 0, lse = -inf for every row (a chunk pair with no keys).
+dfa_status launch_fill_empty(int64_t n_o, float* o, int64_t n_lse, float* lse,
+                             hipStream_t s);
+
+}  // namespace dfa

@@ -24,3 +24,13 @@ def pytest_report_header(config):
 @pytest.fixture(scope="session")
 def repo_root():
     return ROOT
+
+
+@pytest.fixture(scope="session")
+def dfa_lib():
+    """The C-ABI library, built in-tree only if no build exists yet."""
+    from long_context_exact_amd import build as b
+    if not os.path.exists(b.LIB_PATH):
+        b.build()
+    from long_context_exact_amd import dfa
+    return dfa

@@ -1,0 +1,174 @@
+"""CPU checks of the C ABI: the library loads and exports every function the
+header declares, the schedule is bit-exact against the oracle's, and every
+argument check fails cleanly (before any GPU work) with the documented
+status."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import oracle
+from long_context_exact_amd import dfa as D
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "dfa.h")
+FAKE = ctypes.c_void_p(1 << 20)      # never dereferenced: each call below fails validation
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dfa_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(dfa_lib):
+    names = _declared()
+    assert set(names) == set(D.EXPORTED)
+    L = dfa_lib.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", D.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}\b", out), n
+
+
+def test_version(dfa_lib):
+    assert dfa_lib.dfa_version() == 100
+
+
+@pytest.mark.parametrize("p", list(range(1, 65)) + [127, 128, 1000])
+@pytest.mark.parametrize("balanced", [True, False])
+def test_schedule_bit_exact_vs_oracle(dfa_lib, p, balanced):
+    items, steps = dfa_lib.dfa_balanced_schedule(p, balanced)
+    ref, ref_steps = (oracle.balanced_schedule if balanced else oracle.unbalanced_schedule)(p)
+    assert steps == ref_steps
+    assert items == [tuple(x) for x in ref]
+
+
+def test_schedule_argument_errors(dfa_lib):
+    L = dfa_lib.lib()
+    n, s = ctypes.c_int64(-1), ctypes.c_int32(-1)
+    assert L.dfa_balanced_schedule(0, 1, None, 0, ctypes.byref(n), ctypes.byref(s)) == D.DFA_ERR_INVALID
+    assert "num_workers" in dfa_lib.dfa_last_error()
+    assert L.dfa_balanced_schedule(4, 2, None, 0, ctypes.byref(n), ctypes.byref(s)) == D.DFA_ERR_INVALID
+    assert L.dfa_balanced_schedule(4, 1, None, 0, None, ctypes.byref(s)) == D.DFA_ERR_INVALID
+    arr = (D.WorkItem * 3)()
+    assert L.dfa_balanced_schedule(4, 1, arr, 3, ctypes.byref(n), ctypes.byref(s)) == D.DFA_ERR_CAPACITY
+    assert n.value == 10 and s.value == 3
+    assert L.dfa_balanced_schedule(4, 1, None, 0, ctypes.byref(n), ctypes.byref(s)) == D.DFA_ERR_CAPACITY
+    assert n.value == 10
+
+
+def _fwd(L, d, q=FAKE, o=FAKE, lse=FAKE):
+    return L.dfa_attn_fwd_partial(ctypes.byref(d) if d is not None else None, q, FAKE, FAKE, o,
+                                  lse, None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 96, D.DFA_ERR_UNSUPPORTED),
+    ("head_dim", 256, D.DFA_ERR_UNSUPPORTED),
+    ("heads_q", 3, D.DFA_ERR_INVALID),        # not a multiple of heads_kv = 2
+    ("heads_kv", 0, D.DFA_ERR_INVALID),
+    ("len_q", -1, D.DFA_ERR_INVALID),
+    ("kv_start", -5, D.DFA_ERR_INVALID),
+    ("causal", 2, D.DFA_ERR_INVALID),
+    ("scale", -0.5, D.DFA_ERR_INVALID),
+    ("scale", float("inf"), D.DFA_ERR_INVALID),
+    ("dtype", 7, D.DFA_ERR_INVALID),
+    ("batch", -1, D.DFA_ERR_INVALID),
+])
+def test_fwd_descriptor_errors(dfa_lib, field, value, status):
+    L = dfa_lib.lib()
+    d = D.make_desc(1, 4, 2, 128, 256, 256)
+    setattr(d, field, value)
+    assert _fwd(L, d) == status
+    assert dfa_lib.dfa_last_error().startswith("dfa_attn_fwd_partial")
+
+
+def test_fwd_pointer_errors(dfa_lib):
+    L = dfa_lib.lib()
+    d = D.make_desc(1, 4, 2, 128, 256, 256)
+    assert _fwd(L, None) == D.DFA_ERR_INVALID
+    assert _fwd(L, d, q=None) == D.DFA_ERR_INVALID
+    assert _fwd(L, d, lse=None) == D.DFA_ERR_INVALID
+    assert _fwd(L, d, o=ctypes.c_void_p((1 << 20) + 4)) == D.DFA_ERR_INVALID   # misaligned
+    assert "aligned" in dfa_lib.dfa_last_error()
+
+
+def test_empty_problems_enqueue_nothing(dfa_lib):
+    """len_q == 0 and batch == 0 return OK without touching the runtime, so
+    they succeed even with no GPU present."""
+    L = dfa_lib.lib()
+    assert _fwd(L, D.make_desc(1, 2, 2, 64, 0, 128), q=None, o=None, lse=None) == D.DFA_OK
+    assert _fwd(L, D.make_desc(0, 2, 2, 64, 16, 128), q=None, o=None, lse=None) == D.DFA_OK
+
+
+def test_merge_errors(dfa_lib):
+    L = dfa_lib.lib()
+    P = ctypes.c_void_p
+    two = (P * 2)(FAKE, P((1 << 20) + 4096))
+    lses = (P * 2)(FAKE, P((1 << 20) + 8192))
+
+    def merge(n=2, o=two, l=lses, heads=2, hd=64, od=D.DFA_F32, out=P((1 << 21)), lout=P(1 << 22)):
+        return L.dfa_lse_merge(n, o, l, 1, heads, 16, hd, od, out, lout, None)
+
+    assert merge(n=0) == D.DFA_ERR_INVALID
+    assert merge(n=65) == D.DFA_ERR_INVALID
+    assert merge(o=None) == D.DFA_ERR_INVALID
+    assert merge(hd=80) == D.DFA_ERR_UNSUPPORTED
+    assert merge(od=5) == D.DFA_ERR_INVALID
+    assert merge(heads=0) == D.DFA_ERR_INVALID
+    assert merge(out=two[1]) == D.DFA_ERR_INVALID                 # aliases o_parts[1]
+    assert merge(out=two[0], od=D.DFA_BF16) == D.DFA_ERR_INVALID  # bf16 over fp32 input
+    assert merge(lout=lses[1]) == D.DFA_ERR_INVALID
+    assert "alias" in dfa_lib.dfa_last_error()
+
+
+def test_bwd_errors(dfa_lib):
+    L = dfa_lib.lib()
+    d = D.make_desc(1, 2, 2, 64, 64, 64)
+
+    def bwd(desc=d, cd=1, o=FAKE, dq=FAKE):
+        return L.dfa_attn_bwd(ctypes.byref(desc), FAKE, FAKE, FAKE, o, FAKE, FAKE, FAKE, cd, dq,
+                              FAKE, FAKE, None)
+
+    assert bwd(cd=3) == D.DFA_ERR_INVALID
+    assert bwd(o=None) == D.DFA_ERR_INVALID        # compute_delta needs o
+    assert bwd(dq=None) == D.DFA_ERR_INVALID
+    d2 = D.make_desc(1, 2, 2, 32, 64, 64)
+    assert bwd(desc=d2) == D.DFA_ERR_UNSUPPORTED
+
+
+def test_tile_shape_and_visit_guards(dfa_lib):
+    d = D.make_desc(1, 64, 8, 128, 32768, 32768)
+    bm, bn = dfa_lib.dfa_test_tile_shape(d)
+    assert bm >= 32 and bm % 32 == 0 and bn % 32 == 0
+    L = dfa_lib.lib()
+    f = D.make_desc(1, 2, 2, 64, 128, 128, dtype="f32")
+    assert L.dfa_test_fwd_tile_visits(ctypes.byref(f), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      None) == D.DFA_ERR_UNSUPPORTED
+    assert L.dfa_test_fwd_tile_visits(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                      None) == D.DFA_ERR_INVALID
+
+
+def test_runtime_without_device_reports_hip_error(dfa_lib):
+    """With a valid call and no GPU, the launch fails with DFA_ERR_HIP (no
+    crash, no exception across the ABI).  Skipped where a GPU exists: the
+    pointers here are fake."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    L = dfa_lib.lib()
+    assert _fwd(L, D.make_desc(1, 2, 2, 64, 128, 128)) == D.DFA_ERR_HIP
+    assert dfa_lib.dfa_last_error()
+
+
+def test_binding_rejects_mismatched_tensors(dfa_lib):
+    import torch
+    d = D.make_desc(1, 2, 2, 64, 16, 16)
+    cpu = torch.zeros(1, 16, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="HIP device"):
+        dfa_lib.dfa_attn_fwd_partial(d, cpu, cpu, cpu, None, None)
