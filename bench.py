@@ -34,6 +34,35 @@ METRIC = "causal attn fwd+bwd TFLOP/s (1 GPU) at 32K chunk; % of bf16 MFMA peak"
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # MI355X dense MFMA peaks
 
 
+# Profiler names of the kernels the default build launches for bf16 head_dim 128.
+KERNEL_NAMES = {"fwd": "fwd_bf16_kernel", "dkdv": "dkdv_lds_bf16_kernel", "dq": "dq_bf16_kernel"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = {"fwd_bf16_kernel": "fwd_mfma.hip", "dkdv_lds_bf16_kernel": "bwd_mfma.hip",
+                  "dq_bf16_kernel": "bwd_mfma.hip"}
+
+
+def source_digest(name: str) -> str:
+    import hashlib
+    csrc = os.path.join(ROOT, "long_context_exact_amd", "csrc")
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[name], "common.hpp"):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_of(name: str, launches: int):
+    """HBM bytes per launch of `name` from the committed counter summary, or
+    None if there is none or the kernel's sources changed since it was taken."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))["kernels"][name]
+    except (OSError, KeyError, ValueError):
+        return None
+    if t.get("source_digest") != source_digest(name):
+        return None
+    return {"bytes_per_launch": t["bytes_per_launch"], "fetch": t["fetch_bytes_per_launch"],
+            "write": t["write_bytes_per_launch"], "workload": t["workload"]}
+
+
 def pairs_of(kind: int, c: int) -> int:
     return c * (c + 1) // 2 if kind == 0 else c * c
 
@@ -92,6 +121,17 @@ def cpu_baseline(w, host, worker, budget_s):
                       f"{dt:.1f} s, {flops:.3e} algorithmic FLOP"}
 
 
+def copy_calibration(gib: float):
+    import torch
+    n = int(gib * (1 << 30))
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": 3}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -100,7 +140,13 @@ def main():
     ap.add_argument("--workload", default="gqa64x8_512k_w15")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-gib", type=float, default=0.0,
+                    help="only copy this many GiB device-to-device 3 times (the reference kernel "
+                         "whose counter readings calibrate FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
+    if args.copy_gib > 0:
+        copy_calibration(args.copy_gib)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the schedule's "
               "workers are emulated as work items on one device); run with --gpus 1.",
@@ -196,23 +242,32 @@ def main():
         torch.cuda.synchronize()
         return sum(a.elapsed_time(b) for a, b in evs)
 
-    fwd_ms = per_call(lambda it: dfa.dfa_attn_fwd_partial(att.desc(it[2], it[3]), q[it[2]],
-                                                          k[it[3]], v[it[3]],
-                                                          *partials[(it[2], it[3])]), timed)
-    kernels = {"fwd_bf16_kernel": (fwd_ms, fwd_flop, len(timed))}
+    def fwd_call(it):
+        dfa.dfa_attn_fwd_partial(att.desc(it[2], it[3]), q[it[2]], k[it[3]], v[it[3]],
+                                 *partials[(it[2], it[3])])
+
+    def bwd_call(part):
+        return lambda it: dfa.dfa_test_bwd_part(att.desc(it[2], it[3]), q[it[2]], k[it[3]],
+                                                v[it[3]], lse[it[2]], d_o[it[2]], delta[it[2]],
+                                                dq[it[2]], dk[it[3]], dv[it[3]], part)
+
+    pairs_x_heads = sum(pairs_of(it[4], w.chunk) for it in timed) * w.batch * w.heads_q
+    # name in the profiler, time per step, flop per step (the kernel's own
+    # contractions on unmasked pairs: forward 2 = 4d, dK/dV 4 = 8d, dQ 3 = 6d)
+    kernels = {KERNEL_NAMES["fwd"]: (per_call(fwd_call, timed), pairs_x_heads * 4 * w.head_dim)}
     if w.backward:
-        bwd_ms = per_call(lambda it: dfa.dfa_attn_bwd(att.desc(it[2], it[3]), q[it[2]], k[it[3]],
-                                                      v[it[3]], None, lse[it[2]], d_o[it[2]],
-                                                      delta[it[2]], False, dq[it[2]], dk[it[3]],
-                                                      dv[it[3]]), timed)
-        kernels["dkdv_bf16_kernel+dq_bf16_kernel"] = (bwd_ms, bwd_flop, len(timed))
-    name, (kms, kflop, nl) = max(kernels.items(), key=lambda kv: kv[1][0])
+        kernels[KERNEL_NAMES["dkdv"]] = (per_call(bwd_call(1), timed),
+                                         pairs_x_heads * 8 * w.head_dim)
+        kernels[KERNEL_NAMES["dq"]] = (per_call(bwd_call(2), timed),
+                                       pairs_x_heads * 6 * w.head_dim)
+    nl = len(timed)
+    name, (kms, kflop) = max(kernels.items(), key=lambda kv: kv[1][0])
     achieved = kflop / (kms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": name, "achieved": round(achieved, 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
-                "avg_launch_ms": round(kms / nl, 4), "launches_per_step": nl,
-                "algorithmic_flop_per_launch": kflop / nl,
-                "others": {n: {"ms_per_step": round(x[0], 3),
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": traffic_of(name, nl), "avg_launch_ms": round(kms / nl, 3),
+                "launches_per_step": nl, "flop_per_launch": kflop / nl,
+                "others": {n: {"avg_launch_ms": round(x[0] / nl, 3),
                                "tflops": round(x[1] / (x[0] * 1e-3) / 1e12, 2)}
                            for n, x in kernels.items()}}
 

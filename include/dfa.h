@@ -165,6 +165,16 @@ dfa_status dfa_test_fwd_tile_visits(const dfa_attn_desc* desc, const void* q,
                                     float* o_part, float* lse,
                                     uint8_t* visits, void* hip_stream);
 
+/* Runs one of the two kernels that dfa_attn_bwd launches, alone, with the
+ * same arguments and delta already computed: part 1 = the key-outer dK/dV
+ * kernel (dk, dv +=; dq untouched), part 2 = the query-outer dQ kernel
+ * (dq +=; dk, dv untouched).  For timing each kernel on its own. */
+dfa_status dfa_test_bwd_part(const dfa_attn_desc* desc, const void* q,
+                             const void* k, const void* v, const float* lse,
+                             const void* d_o, const float* delta, float* dq,
+                             float* dk, float* dv, int32_t part,
+                             void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -131,33 +131,58 @@ extern "C" dfa_status dfa_lse_merge(int32_t n, const float* const* o_parts,
   }
 }
 
+namespace dfa {
+namespace {
+dfa_status bwd_common(const char* fn, const dfa_attn_desc* desc, const void* q, const void* k,
+                      const void* v, const void* o, const float* lse, const void* d_o,
+                      float* delta, int32_t compute_delta, float* dq, float* dk, float* dv,
+                      void* hip_stream, int parts) {
+  const std::string f(fn);
+  DFA_TRY(check_desc(fn, desc));
+  const dfa_attn_desc& d = *desc;
+  if (compute_delta != 0 && compute_delta != 1)
+    return fail(DFA_ERR_INVALID, f + ": compute_delta must be 0 or 1");
+  if (d.batch == 0 || d.len_q == 0 || d.len_kv == 0) return DFA_OK;  // nothing to add
+  DFA_TRY(need(f, q, "q", true));
+  DFA_TRY(need(f, k, "k", true));
+  DFA_TRY(need(f, v, "v", true));
+  DFA_TRY(need(f, d_o, "d_o", true));
+  DFA_TRY(need(f, lse, "lse", false));
+  DFA_TRY(need(f, delta, "delta", false));
+  if (parts & 2) DFA_TRY(need(f, dq, "dq", true));
+  if (parts & 1) DFA_TRY(need(f, dk, "dk", true));
+  if (parts & 1) DFA_TRY(need(f, dv, "dv", true));
+  if (compute_delta) DFA_TRY(need(f, o, "o", true));
+  const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (compute_delta) DFA_TRY(launch_delta(d, o, d_o, delta, s));
+  return launch_bwd(d, q, k, v, lse, d_o, delta, dq, dk, dv, s, parts);
+}
+}  // namespace
+}  // namespace dfa
+
 extern "C" dfa_status dfa_attn_bwd(const dfa_attn_desc* desc, const void* q, const void* k,
                                    const void* v, const void* o, const float* lse,
                                    const void* d_o, float* delta, int32_t compute_delta,
                                    float* dq, float* dk, float* dv, void* hip_stream) {
   try {
-    const char* fn = "dfa_attn_bwd";
-    const std::string f(fn);
-    DFA_TRY(check_desc(fn, desc));
-    const dfa_attn_desc& d = *desc;
-    if (compute_delta != 0 && compute_delta != 1)
-      return fail(DFA_ERR_INVALID, f + ": compute_delta must be 0 or 1");
-    if (d.batch == 0 || d.len_q == 0 || d.len_kv == 0) return DFA_OK;  // nothing to add
-    DFA_TRY(need(f, q, "q", true));
-    DFA_TRY(need(f, k, "k", true));
-    DFA_TRY(need(f, v, "v", true));
-    DFA_TRY(need(f, d_o, "d_o", true));
-    DFA_TRY(need(f, lse, "lse", false));
-    DFA_TRY(need(f, delta, "delta", false));
-    DFA_TRY(need(f, dq, "dq", true));
-    DFA_TRY(need(f, dk, "dk", true));
-    DFA_TRY(need(f, dv, "dv", true));
-    if (compute_delta) DFA_TRY(need(f, o, "o", true));
-    const hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    if (compute_delta) DFA_TRY(launch_delta(d, o, d_o, delta, s));
-    return launch_bwd(d, q, k, v, lse, d_o, delta, dq, dk, dv, s);
+    return bwd_common("dfa_attn_bwd", desc, q, k, v, o, lse, d_o, delta, compute_delta, dq, dk,
+                      dv, hip_stream, 3);
   } catch (...) {
     return fail(DFA_ERR_INVALID, "dfa_attn_bwd: internal error");
+  }
+}
+
+extern "C" dfa_status dfa_test_bwd_part(const dfa_attn_desc* desc, const void* q, const void* k,
+                                        const void* v, const float* lse, const void* d_o,
+                                        const float* delta, float* dq, float* dk, float* dv,
+                                        int32_t part, void* hip_stream) {
+  try {
+    if (part != 1 && part != 2)
+      return fail(DFA_ERR_INVALID, "dfa_test_bwd_part: part must be 1 or 2");
+    return bwd_common("dfa_test_bwd_part", desc, q, k, v, nullptr, lse, d_o,
+                      const_cast<float*>(delta), 0, dq, dk, dv, hip_stream, part);
+  } catch (...) {
+    return fail(DFA_ERR_INVALID, "dfa_test_bwd_part: internal error");
   }
 }
 

@@ -47,6 +47,57 @@ __device__ __forceinline__ bf16x8 cat4(bf16x4 a, bf16x4 b) {
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+// ---- row-major bf16 tiles in LDS ------------------------------------------
+// A tile holds rows of D bf16 (no padding).  Its 16-byte chunks are XOR-
+// swizzled per row, chunk c of row r stored at c ^ g(r) with
+// g(r) = 2 * (r % 4) + (r / 4) % 2 (low three chunk bits only), so that
+//  * a 16-byte fragment read of one chunk by 8 consecutive rows, and
+//  * a transpose read (below) of 4 consecutive rows x 2 adjacent chunks
+// both touch 8 distinct 16-byte slots of a 128-byte bank line.
+template <int D>
+__device__ __forceinline__ int swz(int row, int chunk) {
+  const int g = ((row & 3) << 1) | ((row >> 2) & 1);
+  return row * D + ((chunk ^ g) << 3);
+}
+
+// LDS pointers carry the LDS address space, so tile addressing stays 32-bit.
+#define DFA_LDS __attribute__((address_space(3)))
+typedef DFA_LDS uint16_t lds_u16;
+typedef DFA_LDS float lds_f32;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ lds_u16* lds_base(uint16_t* generic_smem) {
+  return (lds_u16*)(generic_smem);
+}
+
+// 8 consecutive elements (one chunk) of one row.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+template <int D>
+__device__ __forceinline__ bf16x8 tile_row8(const lds_u16* t, int row, int chunk) {
+  return __builtin_bit_cast(bf16x8, *(const DFA_LDS u32x4*)(t + swz<D>(row, chunk)));
+}
+
+template <int D>
+__device__ __forceinline__ void tile_store16(lds_u16* t, int row, int chunk, uint4 v) {
+  *(DFA_LDS u32x4*)(t + swz<D>(row, chunk)) = u32x4{v.x, v.y, v.z, v.w};
+}
+
+// Transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane j
+// fetches 4 elements at (row0 + j/4, col0 + 4*(j%4)); the hardware returns to
+// lane i the elements (row0 + e, col0 + i), e = 0..3.  So each lane receives
+// 4 consecutive rows of its own column: an MFMA operand whose contraction
+// index runs along the tile's rows.  row0 % 4 == 0, col0 % 16 == 0.
+template <int D>
+__device__ __forceinline__ bf16x4 tile_tr4(const lds_u16* t, int row0, int col0, int lane) {
+  const int j = lane & 15;
+  const int row = row0 + (j >> 2);
+  const int col = col0 + 4 * (j & 3);
+  const lds_u16* p = t + swz<D>(row, col >> 3) + (col & 4);
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DFA_LDS i16x4*)(p));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
 // Round-to-nearest-even fp32 -> bf16 of 8 consecutive accumulator elements.
 __device__ __forceinline__ bf16x8 pack8(const float* p) {
   bf16x8 r;

@@ -202,7 +202,7 @@ dfa_status launch_fwd_f32(const dfa_attn_desc& d, const void* q, const void* k, 
 
 dfa_status launch_bwd_f32(const dfa_attn_desc& d, const void* q, const void* k, const void* v,
                           const float* lse, const void* d_o, const float* delta, float* dq,
-                          float* dk, float* dv, hipStream_t s) {
+                          float* dk, float* dv, hipStream_t s, int parts) {
   F32Args a = make_args(d);
   a.q = static_cast<const float*>(q);
   a.k = static_cast<const float*>(k);
@@ -216,11 +216,11 @@ dfa_status launch_bwd_f32(const dfa_attn_desc& d, const void* q, const void* k, 
   dim3 gq(unsigned(cdiv(d.len_q, 4)), unsigned(d.heads_q), unsigned(d.batch));
   dim3 gk(unsigned(cdiv(d.len_kv, 4)), unsigned(d.heads_kv), unsigned(d.batch));
   if (d.head_dim == 128) {
-    hipLaunchKernelGGL(dq_f32_kernel<128>, gq, dim3(256), 0, s, a);
-    hipLaunchKernelGGL(dkdv_f32_kernel<128>, gk, dim3(256), 0, s, a);
+    if (parts & 2) hipLaunchKernelGGL(dq_f32_kernel<128>, gq, dim3(256), 0, s, a);
+    if (parts & 1) hipLaunchKernelGGL(dkdv_f32_kernel<128>, gk, dim3(256), 0, s, a);
   } else {
-    hipLaunchKernelGGL(dq_f32_kernel<64>, gq, dim3(256), 0, s, a);
-    hipLaunchKernelGGL(dkdv_f32_kernel<64>, gk, dim3(256), 0, s, a);
+    if (parts & 2) hipLaunchKernelGGL(dq_f32_kernel<64>, gq, dim3(256), 0, s, a);
+    if (parts & 1) hipLaunchKernelGGL(dkdv_f32_kernel<64>, gk, dim3(256), 0, s, a);
   }
   return check_launch("dq_f32_kernel / dkdv_f32_kernel");
 }

@@ -21,10 +21,11 @@ dfa_status launch_merge(int32_t n, const float* const* o_parts,
 dfa_status launch_delta(const dfa_attn_desc& d, const void* o, const void* d_o,
                         float* delta, hipStream_t s);
 
+// parts: bit 0 = dK/dV kernel, bit 1 = dQ kernel (3 = the whole backward).
 dfa_status launch_bwd(const dfa_attn_desc& d, const void* q, const void* k,
                       const void* v, const float* lse, const void* d_o,
                       const float* delta, float* dq, float* dk, float* dv,
-                      hipStream_t s);
+                      hipStream_t s, int parts = 3);
 
 // o = 0, lse = -inf for every row (a chunk pair with no keys).
 dfa_status launch_fill_empty(int64_t n_o, float* o, int64_t n_lse, float* lse,

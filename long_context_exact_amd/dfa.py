@@ -29,6 +29,7 @@ _TORCH = {DFA_F32: torch.float32, DFA_BF16: torch.bfloat16}
 EXPORTED = (
     "dfa_balanced_schedule", "dfa_attn_fwd_partial", "dfa_lse_merge", "dfa_attn_bwd",
     "dfa_last_error", "dfa_version", "dfa_test_tile_shape", "dfa_test_fwd_tile_visits",
+    "dfa_test_bwd_part",
 )
 
 
@@ -84,8 +85,11 @@ def lib() -> ctypes.CDLL:
         L.dfa_test_tile_shape.argtypes = [ctypes.POINTER(AttnDesc), ctypes.POINTER(I32),
                                           ctypes.POINTER(I32)]
         L.dfa_test_fwd_tile_visits.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P]
+        L.dfa_test_bwd_part.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, P, P, I32,
+                                        P]
         for name in ("dfa_balanced_schedule", "dfa_attn_fwd_partial", "dfa_lse_merge",
-                     "dfa_attn_bwd", "dfa_test_tile_shape", "dfa_test_fwd_tile_visits"):
+                     "dfa_attn_bwd", "dfa_test_tile_shape", "dfa_test_fwd_tile_visits",
+                     "dfa_test_bwd_part"):
             getattr(L, name).restype = I32
         L.dfa_last_error.argtypes = []
         L.dfa_last_error.restype = ctypes.c_char_p
@@ -206,3 +210,17 @@ def dfa_test_fwd_tile_visits(desc: AttnDesc, q, k, v, o_part, lse, visits, strea
             _ptr(o_part, "o_part", qs, torch.float32), _ptr(lse, "lse", ls, torch.float32),
             _ptr(visits, "visits", vshape, torch.uint8))
     _check(lib().dfa_test_fwd_tile_visits(ctypes.byref(desc), *args, _stream(stream)))
+
+
+def dfa_test_bwd_part(desc: AttnDesc, q, k, v, lse, d_o, delta, dq, dk, dv, part: int,
+                      stream=None):
+    """One backward kernel alone (1: dK/dV, 2: dQ), delta already computed."""
+    qs, ks, ls = _shapes(desc)
+    dt = _TORCH.get(desc.dtype, torch.bfloat16)
+    f32 = torch.float32
+    args = (_ptr(q, "q", qs, dt), _ptr(k, "k", ks, dt), _ptr(v, "v", ks, dt),
+            _ptr(lse, "lse", ls, f32), _ptr(d_o, "d_o", qs, dt), _ptr(delta, "delta", ls, f32),
+            _ptr(dq, "dq", qs, f32) if part == 2 else None,
+            _ptr(dk, "dk", ks, f32) if part == 1 else None,
+            _ptr(dv, "dv", ks, f32) if part == 1 else None)
+    _check(lib().dfa_test_bwd_part(ctypes.byref(desc), *args, int(part), _stream(stream)))
