@@ -18,6 +18,9 @@
 //      S^T = K Q^T, dP^T = V dO^T          (lane = query row)
 //      dS^T = P^T (dP^T - delta),  dQ^T += K^T dS^T
 // Both add into the caller's fp32 accumulators (dq, dk, dv +=).
+#include <algorithm>
+#include <cfloat>
+
 #include "kernels.hpp"
 
 namespace dfa {
@@ -36,7 +39,7 @@ struct BwdArgs {
   int64_t len_q, len_kv, q_start, kv_start;
   int32_t hq, hkv, group, causal;
   int32_t n_tiles, n_hgroups, n_ktiles;
-  float c;      // scale * log2(e)
+  float c;      // scale * log2(e), > 0
   float scale;
 };
 
@@ -68,7 +71,8 @@ __global__ __launch_bounds__(NW * 64) void dkdv_bf16_kernel(BwdArgs a) {
   lds_u16* smem = lds_base(smem_generic);
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+  const int lane = tid & 63;
   const int l32 = lane & 31, hi = lane >> 5;
   const int half16 = (lane >> 4) & 1;
   const int kt = blockIdx.x / a.hkv;
@@ -187,6 +191,13 @@ __global__ __launch_bounds__(NW * 64) void dkdv_bf16_kernel(BwdArgs a) {
       const int64_t rmin = a.causal ? a.kv_start + key - a.q_start - r0 : INT64_MIN / 2;
       const int64_t rmax = a.len_q - 1 - r0;
       const bool key_ok = key < a.len_kv;
+      if (need_mask) {  // hidden scores -> -inf, so P = exp2(-inf) = 0 (c > 0)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ri = 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (!key_ok || ri < rmin || ri > rmax) s[r] = -INFINITY;
+        }
+      }
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const f32x4 x = *(const DFA_LDS f32x4*)(lse2s + 32 * qb + 8 * r4 + 4 * hi);
@@ -194,11 +205,7 @@ __global__ __launch_bounds__(NW * 64) void dkdv_bf16_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * r4 + e;
-          float p = exp2_fast(fmaf(s[r], a.c, -x[e]));
-          if (need_mask) {
-            const int ri = 8 * r4 + 4 * hi + e;
-            if (!key_ok || ri < rmin || ri > rmax) p = 0.f;
-          }
+          const float p = exp2_fast(fmaf(s[r], a.c, -x[e]));
           s[r] = p;
           dp[r] = p * (dp[r] - y[e]);
         }
@@ -284,7 +291,8 @@ void dkdv_lds_bf16_kernel(BwdArgs a) {
   lds_f32* dls = lse2s + C::BQ;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+  const int lane = tid & 63;
   const int l32 = lane & 31, hi = lane >> 5;
   const int half16 = (lane >> 4) & 1;
   const int kt = blockIdx.x / a.hkv;
@@ -393,6 +401,13 @@ void dkdv_lds_bf16_kernel(BwdArgs a) {
       const int64_t rmin = a.causal ? a.kv_start + key - a.q_start - r0 : INT64_MIN / 2;
       const int64_t rmax = a.len_q - 1 - r0;
       const bool key_ok = key < a.len_kv;
+      if (need_mask) {  // hidden scores -> -inf, so P = exp2(-inf) = 0 (c > 0)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ri = 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (!key_ok || ri < rmin || ri > rmax) s[r] = -INFINITY;
+        }
+      }
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const f32x4 x = *(const DFA_LDS f32x4*)(lse2s + 8 * r4 + 4 * hi);
@@ -400,11 +415,7 @@ void dkdv_lds_bf16_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * r4 + e;
-          float p = exp2_fast(fmaf(s[r], a.c, -x[e]));
-          if (need_mask) {
-            const int ri = 8 * r4 + 4 * hi + e;
-            if (!key_ok || ri < rmin || ri > rmax) p = 0.f;
-          }
+          const float p = exp2_fast(fmaf(s[r], a.c, -x[e]));
           s[r] = p;
           dp[r] = p * (dp[r] - y[e]);
         }
@@ -478,7 +489,8 @@ void dq_bf16_kernel(BwdArgs a) {
   lds_u16* smem = lds_base(smem_generic);
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+  const int lane = tid & 63;
   const int l32 = lane & 31, hi = lane >> 5;
   const int half16 = (lane >> 4) & 1;
   const int bid = blockIdx.x;
@@ -589,13 +601,16 @@ void dq_bf16_kernel(BwdArgs a) {
             s = mfma32(tile_row8<D>(Ks, kb * 32 + l32, 2 * st + hi), qf[st], s);
             dp = mfma32(tile_row8<D>(Vs, kb * 32 + l32, 2 * st + hi), df[st], dp);
           }
+          if (need_mask) {  // hidden scores -> -inf, so P = exp2(-inf) = 0 (c > 0)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int off = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+              if (off > vlim) s[r] = -INFINITY;
+            }
+          }
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            float p = exp2_fast(fmaf(s[r], a.c, -lse2));
-            if (need_mask) {
-              const int off = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-              if (off > vlim) p = 0.f;
-            }
+            const float p = exp2_fast(fmaf(s[r], a.c, -lse2));
             dp[r] = p * (dp[r] - dl);
           }
 #pragma unroll
@@ -645,15 +660,6 @@ constexpr int kDqBN = 64;
 constexpr int kDkvNW = 4;
 constexpr int kDkvBQ = 64;
 
-// Opt a kernel into more than 64 KiB of dynamic LDS (gfx950 has 160 KiB).
-template <typename K>
-dfa_status allow_lds(K kernel, int bytes, const char* what) {
-  if (bytes <= 65536) return DFA_OK;
-  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
-  return DFA_OK;
-}
 
 template <int D, int NW, int HPW>
 dfa_status launch_dq(const dfa_attn_desc& d, BwdArgs a, hipStream_t s) {
@@ -732,7 +738,10 @@ dfa_status launch_bwd(const dfa_attn_desc& d, const void* q, const void* k, cons
   a.hkv = d.heads_kv;
   a.group = d.heads_q / d.heads_kv;
   a.causal = d.causal;
-  a.c = d.scale * kLog2e;
+  // c > 0 keeps exp2(fma(-inf, c, -lse2)) == 0 for hidden scores; a zero
+  // scale runs as the smallest normal one (scores * 1.2e-38 round away in
+  // fp32), and dQ, dK carry the true scale.
+  a.c = std::max(d.scale * kLog2e, FLT_MIN);
   a.scale = d.scale;
   if (d.head_dim == 128) return launch_bwd_d<128>(d, a, s, parts);
   return launch_bwd_d<64>(d, a, s, parts);

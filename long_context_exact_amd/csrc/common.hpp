@@ -48,15 +48,22 @@ __device__ __forceinline__ bf16x8 cat4(bf16x4 a, bf16x4 b) {
 }
 
 // ---- row-major bf16 tiles in LDS ------------------------------------------
-// A tile holds rows of D bf16 (no padding).  Its 16-byte chunks are XOR-
-// swizzled per row, chunk c of row r stored at c ^ g(r) with
-// g(r) = 2 * (r % 4) + (r / 4) % 2 (low three chunk bits only), so that
-//  * a 16-byte fragment read of one chunk by 8 consecutive rows, and
-//  * a transpose read (below) of 4 consecutive rows x 2 adjacent chunks
-// both touch 8 distinct 16-byte slots of a 128-byte bank line.
+// A tile holds rows of D bf16 (no padding).  gfx950's LDS serves 256 bytes
+// (64 four-byte banks) per cycle, so its 16-byte chunks are XOR-swizzled per
+// row such that
+//  * a 16-byte fragment read of one chunk by 16 consecutive rows (16 lanes),
+//  * a transpose read (below) of 4 consecutive rows x 4 adjacent chunks
+//    (32 lanes), and
+//  * a 16-byte store of 16 consecutive chunks of one row
+// each touch 16 distinct 16-byte slots of a 256-byte bank line.
+//   D = 128 (16 chunks, one row per line):  chunk c of row r at c ^ g,
+//     g = 4 * (r % 4) + (r / 4) % 4;
+//   D = 64 (8 chunks, two rows per line):   g = 4 * ((r / 2) % 2) + (r / 4) % 4.
 template <int D>
 __device__ __forceinline__ int swz(int row, int chunk) {
-  const int g = ((row & 3) << 1) | ((row >> 2) & 1);
+  static_assert(D == 64 || D == 128, "tile rows of 64 or 128 elements");
+  const int g = D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3))
+                         : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
   return row * D + ((chunk ^ g) << 3);
 }
 
@@ -97,6 +104,28 @@ __device__ __forceinline__ bf16x4 tile_tr4(const lds_u16* t, int row0, int col0,
   const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DFA_LDS i16x4*)(p));
   return __builtin_bit_cast(bf16x4, r);
 }
+
+// Direct global -> LDS staging of a swizzled tile (global_load_lds_dwordx4):
+// lane i of a wave writes the 16 bytes at LDS byte address M0 + 16 * i, so a
+// wave fills one 1 KiB segment per instruction; to land chunk c of row r at
+// its swizzled slot, the lane whose slot is (r, p) loads the global chunk
+// c = p ^ g(r).  `seg` is the segment index inside the tile; `row_ptr(r)`
+// gives the global address of the tile's row r (already clamped in range).
+template <int D, typename RowPtr>
+__device__ __forceinline__ void tile_dma_segment(lds_u16* tile, int seg, int lane, RowPtr row_ptr) {
+  constexpr int ROWS_PER_SEG = 512 / D;    // 1 KiB / (2 bytes * D)
+  constexpr int CHUNKS = D / 8;
+  const int row = seg * ROWS_PER_SEG + lane / CHUNKS;
+  const int phys = lane % CHUNKS;
+  // logical chunk whose swizzled slot is `phys` (g is an involution partner)
+  const int logical = (swz<D>(row, phys) - row * D) >> 3;
+  const uint16_t* src = row_ptr(row) + 8 * logical;
+  typedef DFA_LDS void lds_void;
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)(tile + seg * 512), 16, 0, 0);
+}
+
+// Wait for this wave's outstanding global loads (including LDS-direct ones).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Round-to-nearest-even fp32 -> bf16 of 8 consecutive accumulator elements.
 __device__ __forceinline__ bf16x8 pack8(const float* p) {

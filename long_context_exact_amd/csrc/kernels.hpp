@@ -27,6 +27,24 @@ dfa_status launch_bwd(const dfa_attn_desc& d, const void* q, const void* k,
                       const float* delta, float* dq, float* dk, float* dv,
                       hipStream_t s, int parts = 3);
 
+// Opt a kernel into more than 64 KiB of dynamic LDS (gfx950 has 160 KiB).
+template <typename K>
+dfa_status allow_lds(K kernel, int bytes, const char* what) {
+  if (bytes <= 65536) return DFA_OK;
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return fail(DFA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return DFA_OK;
+}
+
+// True when every query row of the pair sees every key (non-causal, or the
+// key chunk ends at or before the first query) and the key chunk is a whole
+// number of `tile` keys: such pairs need no mask anywhere.
+inline bool pair_is_full(const dfa_attn_desc& d, int64_t tile) {
+  const bool all_visible = !d.causal || d.kv_start + d.len_kv - 1 <= d.q_start;
+  return all_visible && d.len_kv % tile == 0;
+}
+
 // o = 0, lse = -inf for every row (a chunk pair with no keys).
 dfa_status launch_fill_empty(int64_t n_o, float* o, int64_t n_lse, float* lse,
                              hipStream_t s);
