@@ -35,9 +35,9 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # MI355X dense MFMA peaks
 
 
 # Profiler names of the kernels the default build launches for bf16 head_dim 128.
-KERNEL_NAMES = {"fwd": "fwd_bf16_kernel", "dkdv": "dkdv_lds_bf16_kernel", "dq": "dq_bf16_kernel"}
+KERNEL_NAMES = {"fwd": "fwd_bf16_kernel", "dkdv": "dkdv_bf16_kernel", "dq": "dq_bf16_kernel"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-KERNEL_SOURCES = {"fwd_bf16_kernel": "fwd_mfma.hip", "dkdv_lds_bf16_kernel": "bwd_mfma.hip",
+KERNEL_SOURCES = {"fwd_bf16_kernel": "fwd_mfma.hip", "dkdv_bf16_kernel": "bwd_mfma.hip",
                   "dq_bf16_kernel": "bwd_mfma.hip"}
 
 

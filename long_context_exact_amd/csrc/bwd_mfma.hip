@@ -6,10 +6,10 @@
 //
 // Two deterministic kernels, each owning its outputs (no atomics):
 //  dkdv_bf16_kernel  key-outer.  A workgroup owns 32*NW keys of one
-//    key/value head; wave w owns 32 of them with K, V held as MFMA operands
-//    in VGPRs and dK^T, dV^T accumulated in VGPRs over every query head of
-//    the group and every query row that sees the keys.  Per step of BQ
-//    query rows (Q, dO row-major and swizzled in LDS, double-buffered):
+//    key/value head (their K and V rows resident in LDS); wave w owns 32 of
+//    them and accumulates dK^T, dV^T in VGPRs over every query head of the
+//    group and every query row that sees the keys.  Per step of 32 query
+//    rows (Q, dO staged straight from HBM into swizzled LDS, double-buffered):
 //      S  = Q K^T,  dP = dO V^T            (lane = key, registers = rows)
 //      P  = exp2(S*c - LSE2),  dS = P (dP - delta)
 //      dV^T += dO^T P,  dK^T += Q^T dS     (A operand via transpose reads,
@@ -17,7 +17,10 @@
 //  dq_bf16_kernel    query-outer, shaped like the forward.  Per key tile:
 //      S^T = K Q^T, dP^T = V dO^T          (lane = query row)
 //      dS^T = P^T (dP^T - delta),  dQ^T += K^T dS^T
-// Both add into the caller's fp32 accumulators (dq, dk, dv +=).
+// Both add into the caller's fp32 accumulators (dq, dk, dv +=).  Pairs in
+// which every query sees every key run mask-free instantiations (in dQ the
+// key loop is also software-pipelined: the next block's S and dP are issued
+// next to the current block's vector work).
 #include <algorithm>
 #include <cfloat>
 
@@ -49,246 +52,41 @@ __device__ __forceinline__ float lse2_of(float lse) {
   return lse > -INFINITY ? lse * kLog2e : INFINITY;
 }
 
-// ---------------------------------------------------------------- dK, dV
-template <int D, int NW, int BQ>
-struct DkvCfg {
-  static constexpr int NT = NW * 64;
-  static constexpr int BK = 32 * NW;   // keys per workgroup
-  static constexpr int CH = BQ * D / 8;
-  static constexpr int CPT = CH / NT;
-  static constexpr int TILE = BQ * D;  // elements of one Q (or dO) tile
-  // stage: Q tile, dO tile, then BQ floats of LSE2 and BQ floats of delta
-  static constexpr int STAGE_BYTES = 2 * TILE * 2 + 2 * BQ * 4;
-  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
-  static_assert(CH % NT == 0, "query tile chunks must divide evenly");
-  static_assert(2 * BQ <= NT, "one thread per LSE / delta value");
-};
-
-template <int D, int NW, int BQ>
-__global__ __launch_bounds__(NW * 64) void dkdv_bf16_kernel(BwdArgs a) {
-  using C = DkvCfg<D, NW, BQ>;
-  extern __shared__ __align__(16) uint16_t smem_generic[];
-  lds_u16* smem = lds_base(smem_generic);
-
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
-  const int lane = tid & 63;
-  const int l32 = lane & 31, hi = lane >> 5;
-  const int half16 = (lane >> 4) & 1;
-  const int kt = blockIdx.x / a.hkv;
-  const int g = blockIdx.x % a.hkv;
-  const int64_t b = blockIdx.y;
-  const int64_t k_lo = int64_t(kt) * C::BK;
-  const int64_t wk_lo = k_lo + wave * 32;
-  const int64_t wk_hi = min(wk_lo + 32, a.len_kv);
-  const bool wave_active = wk_lo < a.len_kv;
-  const int64_t key = wk_lo + l32;
-
-  const int64_t q_rs = int64_t(a.hq) * D;
-  const int64_t kv_rs = int64_t(a.hkv) * D;
-
-  bf16x8 kf[D / 16], vf[D / 16];
-  {
-    const uint16_t* kp = a.k + (b * a.len_kv + key) * kv_rs + int64_t(g) * D;
-    const uint16_t* vp = a.v + (b * a.len_kv + key) * kv_rs + int64_t(g) * D;
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st) {
-      if (key < a.len_kv) {
-        kf[st] = ld_bf16x8(kp + 16 * st + 8 * hi);
-        vf[st] = ld_bf16x8(vp + 16 * st + 8 * hi);
-      } else {
-        kf[st] = bf16x8{};
-        vf[st] = bf16x8{};
-      }
-    }
-  }
-
-  // Query rows that see at least one key of this workgroup.
-  int64_t i_begin = 0;
-  if (a.causal) i_begin = max<int64_t>(0, a.kv_start + k_lo - a.q_start);
-  if (i_begin >= a.len_q) return;  // uniform over the workgroup
-  const int qt0 = int(i_begin / BQ);
-  const int nq = int(cdiv(a.len_q, BQ)) - qt0;
-  const int steps = a.group * nq;
-
-  f32x16 dk_acc[D / 32], dv_acc[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
-    dk_acc[db] = f32x16{};
-    dv_acc[db] = f32x16{};
-  }
-
-  uint4 qreg[C::CPT], dreg[C::CPT];
-  float sreg = 0.f;
-  auto gload = [&](int it) {
-    const int h = g * a.group + it / nq;
-    const int64_t i0 = int64_t(qt0 + it % nq) * BQ;
-    const uint16_t* qb = a.q + b * a.len_q * q_rs + int64_t(h) * D;
-    const uint16_t* db_ = a.d_o + b * a.len_q * q_rs + int64_t(h) * D;
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int c = tid + i * C::NT;
-      const int r = c / (D / 8), dc = c % (D / 8);
-      const int64_t row = i0 + r;
-      if (row < a.len_q) {
-        qreg[i] = ld_u4(qb + row * q_rs + 8 * dc);
-        dreg[i] = ld_u4(db_ + row * q_rs + 8 * dc);
-      } else {
-        qreg[i] = make_uint4(0, 0, 0, 0);
-        dreg[i] = make_uint4(0, 0, 0, 0);
-      }
-    }
-    if (tid < 2 * BQ) {
-      const int64_t row = i0 + (tid % BQ);
-      const int64_t li = (b * a.hq + h) * a.len_q + row;
-      if (tid < BQ) sreg = row < a.len_q ? lse2_of(a.lse[li]) : INFINITY;
-      else sreg = row < a.len_q ? a.delta[li] : 0.f;
-    }
-  };
-  auto stage_ptr = [&](int stage) {
-    return smem + stage * (C::STAGE_BYTES / 2);
-  };
-  auto sstore = [&](int stage) {
-    lds_u16* Qs = stage_ptr(stage);
-    lds_u16* dOs = Qs + C::TILE;
-    lds_f32* sv = (lds_f32*)(dOs + C::TILE);
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int c = tid + i * C::NT;
-      const int r = c / (D / 8), dc = c % (D / 8);
-      tile_store16<D>(Qs, r, dc, qreg[i]);
-      tile_store16<D>(dOs, r, dc, dreg[i]);
-    }
-    if (tid < 2 * BQ) sv[tid] = sreg;
-  };
-
-  gload(0);
-  sstore(0);
-  __syncthreads();
-
-  for (int it = 0; it < steps; ++it) {
-    if (it + 1 < steps) gload(it + 1);
-    const lds_u16* Qs = stage_ptr(it & 1);
-    const lds_u16* dOs = Qs + C::TILE;
-    const lds_f32* lse2s = (const lds_f32*)(dOs + C::TILE);
-    const lds_f32* dls = lse2s + BQ;
-    const int64_t i0 = int64_t(qt0 + it % nq) * BQ;
-#pragma unroll 1
-    for (int qb = 0; qb < BQ / 32; ++qb) {
-      const int64_t r0 = i0 + 32 * qb;  // first row of this 32-row block
-      bool any = wave_active && r0 < a.len_q;
-      if (any && a.causal) any = a.q_start + min(r0 + 32, a.len_q) - 1 >= a.kv_start + wk_lo;
-      if (!any) continue;
-      const bool need_mask = (a.causal && a.q_start + r0 < a.kv_start + wk_hi - 1) ||
-                             (r0 + 32 > a.len_q) || (wk_lo + 32 > a.len_kv);
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int st = 0; st < D / 16; ++st) {
-        s = mfma32(tile_row8<D>(Qs, 32 * qb + l32, 2 * st + hi), kf[st], s);
-        dp = mfma32(tile_row8<D>(dOs, 32 * qb + l32, 2 * st + hi), vf[st], dp);
-      }
-      // row (local to the block) of register r: 8 * (r / 4) + 4 * hi + r % 4
-      const int64_t rmin = a.causal ? a.kv_start + key - a.q_start - r0 : INT64_MIN / 2;
-      const int64_t rmax = a.len_q - 1 - r0;
-      const bool key_ok = key < a.len_kv;
-      if (need_mask) {  // hidden scores -> -inf, so P = exp2(-inf) = 0 (c > 0)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ri = 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (!key_ok || ri < rmin || ri > rmax) s[r] = -INFINITY;
-        }
-      }
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 x = *(const DFA_LDS f32x4*)(lse2s + 32 * qb + 8 * r4 + 4 * hi);
-        const f32x4 y = *(const DFA_LDS f32x4*)(dls + 32 * qb + 8 * r4 + 4 * hi);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * r4 + e;
-          const float p = exp2_fast(fmaf(s[r], a.c, -x[e]));
-          s[r] = p;
-          dp[r] = p * (dp[r] - y[e]);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        bf16x8 pb, sb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pb[e] = static_cast<__bf16>(s[8 * j + e]);
-          sb[e] = static_cast<__bf16>(dp[8 * j + e]);
-        }
-        const int t0 = 32 * qb + 16 * j + 4 * hi;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const int c0 = 32 * db + 16 * half16;
-          const bf16x8 ta =
-              cat4(tile_tr4<D>(dOs, t0, c0, lane), tile_tr4<D>(dOs, t0 + 8, c0, lane));
-          dv_acc[db] = mfma32(ta, pb, dv_acc[db]);
-          const bf16x8 ua = cat4(tile_tr4<D>(Qs, t0, c0, lane), tile_tr4<D>(Qs, t0 + 8, c0, lane));
-          dk_acc[db] = mfma32(ua, sb, dk_acc[db]);
-        }
-      }
-    }
-    if (it + 1 < steps) sstore((it + 1) & 1);
-    __syncthreads();
-  }
-
-  if (!wave_active || key >= a.len_kv) return;
-  float* dkr = a.dk + (b * a.len_kv + key) * kv_rs + int64_t(g) * D;
-  float* dvr = a.dv + (b * a.len_kv + key) * kv_rs + int64_t(g) * D;
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int d = 32 * db + 8 * r4 + 4 * hi;
-      f32x4 xk = *reinterpret_cast<f32x4*>(dkr + d);
-      f32x4 xv = *reinterpret_cast<f32x4*>(dvr + d);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        xk[e] += a.scale * dk_acc[db][4 * r4 + e];
-        xv[e] += dv_acc[db][4 * r4 + e];
-      }
-      *reinterpret_cast<f32x4*>(dkr + d) = xk;
-      *reinterpret_cast<f32x4*>(dvr + d) = xv;
-    }
-}
-
-// Variant of the key-outer kernel for two waves per SIMD: the workgroup's
-// K and V rows live in LDS (read as MFMA operands) instead of VGPRs, which
-// leaves the register budget to the dK^T / dV^T accumulators.  NW waves own
-// 32*NW keys; steps of 32 query rows, single-buffered with a register
-// prefetch of the next step.
-template <int D, int NW>
-struct DkvLdsCfg {
-  static constexpr int NT = NW * 64;
-  static constexpr int BK = 32 * NW;
-  static constexpr int BQ = 32;
-  static constexpr int KV_TILE = BK * D;   // elements of the K (or V) tile
-  static constexpr int Q_TILE = BQ * D;
-  static constexpr int LDS_BYTES = (2 * KV_TILE + 2 * Q_TILE) * 2 + 2 * BQ * 4;
-  static constexpr int QCPT = Q_TILE / 8 / NT;   // 16-byte chunks per thread (Q or dO)
-  static constexpr int KCPT = KV_TILE / 8 / NT;  // chunks per thread (K or V)
-  static_assert(QCPT >= 1 && Q_TILE / 8 % NT == 0, "query chunks must divide evenly");
-  static_assert(KV_TILE / 8 % NT == 0, "key chunks must divide evenly");
-};
-
-#ifndef DFA_DKDV_OCC
-#define DFA_DKDV_OCC 2
+#ifndef DFA_BWD_OCC
+#define DFA_BWD_OCC 2  // waves per SIMD the register budget is sized for
 #endif
 
+// ---------------------------------------------------------------- dK, dV
+// The workgroup's K and V rows stay in LDS for the whole run (MFMA B operands
+// read per block), Q and dO come in double-buffered 32-row stages, and each
+// lane reads the LSE / delta of its 16 rows straight from memory (tiny and
+// L2-resident; the block's 16 S / dP instructions cover the latency).  This
+// fills exactly 160 KiB of LDS and leaves the register budget of two waves
+// per SIMD to the dK^T / dV^T accumulators.
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DFA_DKDV_OCC, DFA_DKDV_OCC)))
-void dkdv_lds_bf16_kernel(BwdArgs a) {
-  using C = DkvLdsCfg<D, NW>;
+struct DkvCfg {
+  static constexpr int NT = NW * 64;
+  static constexpr int BK = 32 * NW;            // keys per workgroup
+  static constexpr int BQ = 32;                 // query rows per step
+  static constexpr int KV_TILE = BK * D;        // elements of the K (or V) tile
+  static constexpr int KV_SEGS = KV_TILE / 512; // 1 KiB segments
+  static constexpr int Q_TILE = BQ * D;         // elements of one Q (or dO) tile
+  static constexpr int Q_SEGS = Q_TILE / 512;
+  static constexpr int STAGE = 2 * Q_TILE;      // Q + dO (elements)
+  static constexpr int LDS_BYTES = (2 * KV_TILE + 2 * STAGE) * 2;
+  static_assert(KV_SEGS % NW == 0, "key tile segments must divide over the waves");
+  static_assert(Q_SEGS % NW == 0 || NW % Q_SEGS == 0, "query segments over the waves");
+  static_assert(LDS_BYTES <= 160 * 1024, "fits gfx950 LDS");
+};
+
+template <int D, int NW, bool FULL>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DFA_BWD_OCC, DFA_BWD_OCC)))
+void dkdv_bf16_kernel(BwdArgs a) {
+  using C = DkvCfg<D, NW>;
   extern __shared__ __align__(16) uint16_t smem_generic[];
   lds_u16* smem = lds_base(smem_generic);
   lds_u16* Ks = smem;
   lds_u16* Vs = Ks + C::KV_TILE;
-  lds_u16* Qs = Vs + C::KV_TILE;
-  lds_u16* dOs = Qs + C::Q_TILE;
-  lds_f32* lse2s = (lds_f32*)(dOs + C::Q_TILE);
-  lds_f32* dls = lse2s + C::BQ;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
@@ -307,6 +105,7 @@ void dkdv_lds_bf16_kernel(BwdArgs a) {
   const int64_t q_rs = int64_t(a.hq) * D;
   const int64_t kv_rs = int64_t(a.hkv) * D;
 
+  // Query rows that see at least one key of this workgroup.
   int64_t i_begin = 0;
   if (a.causal) i_begin = max<int64_t>(0, a.kv_start + k_lo - a.q_start);
   if (i_begin >= a.len_q) return;  // uniform over the workgroup
@@ -314,22 +113,19 @@ void dkdv_lds_bf16_kernel(BwdArgs a) {
   const int nq = int(cdiv(a.len_q, C::BQ)) - qt0;
   const int steps = a.group * nq;
 
-  // The workgroup's K and V rows, once.
-  {
+  {  // the workgroup's K and V rows, once
     const uint16_t* kb = a.k + b * a.len_kv * kv_rs + int64_t(g) * D;
     const uint16_t* vb = a.v + b * a.len_kv * kv_rs + int64_t(g) * D;
-#pragma unroll 1
-    for (int i = 0; i < C::KCPT; ++i) {
-      const int c = tid + i * C::NT;
-      const int r = c / (D / 8), dc = c % (D / 8);
-      const int64_t kk = k_lo + r;
-      uint4 x = make_uint4(0, 0, 0, 0), y = make_uint4(0, 0, 0, 0);
-      if (kk < a.len_kv) {
-        x = ld_u4(kb + kk * kv_rs + 8 * dc);
-        y = ld_u4(vb + kk * kv_rs + 8 * dc);
-      }
-      tile_store16<D>(Ks, r, dc, x);
-      tile_store16<D>(Vs, r, dc, y);
+    const int64_t last = a.len_kv - 1;  // rows past the chunk re-read its last key (masked)
+#pragma unroll
+    for (int i = 0; i < C::KV_SEGS / NW; ++i) {
+      const int seg = wave * (C::KV_SEGS / NW) + i;
+      tile_dma_segment<D>(Ks, seg, lane, [&](int r) {
+        return kb + min<int64_t>(k_lo + r, last) * kv_rs;
+      });
+      tile_dma_segment<D>(Vs, seg, lane, [&](int r) {
+        return vb + min<int64_t>(k_lo + r, last) * kv_rs;
+      });
     }
   }
 
@@ -340,68 +136,78 @@ void dkdv_lds_bf16_kernel(BwdArgs a) {
     dv_acc[db] = f32x16{};
   }
 
-  uint4 qreg[C::QCPT], dreg[C::QCPT];
-  float sreg = 0.f;
-  auto gload = [&](int it) {
+  auto stage_ptr = [&](int stage) { return smem + 2 * C::KV_TILE + stage * C::STAGE; };
+  auto stage_q = [&](int it, int stage) {
     const int h = g * a.group + it / nq;
     const int64_t i0 = int64_t(qt0 + it % nq) * C::BQ;
     const uint16_t* qb = a.q + b * a.len_q * q_rs + int64_t(h) * D;
     const uint16_t* db_ = a.d_o + b * a.len_q * q_rs + int64_t(h) * D;
-#pragma unroll
-    for (int i = 0; i < C::QCPT; ++i) {
-      const int c = tid + i * C::NT;
-      const int r = c / (D / 8), dc = c % (D / 8);
-      const int64_t row = i0 + r;
-      if (row < a.len_q) {
-        qreg[i] = ld_u4(qb + row * q_rs + 8 * dc);
-        dreg[i] = ld_u4(db_ + row * q_rs + 8 * dc);
-      } else {
-        qreg[i] = make_uint4(0, 0, 0, 0);
-        dreg[i] = make_uint4(0, 0, 0, 0);
-      }
+    lds_u16* Qs = stage_ptr(stage);
+    lds_u16* dOs = Qs + C::Q_TILE;
+    const int64_t last = a.len_q - 1;  // rows past the chunk re-read its last row (P = 0)
+    // 2 * Q_SEGS segments (Q then dO) spread over the waves
+    for (int seg = wave; seg < 2 * C::Q_SEGS; seg += NW) {
+      if (seg < C::Q_SEGS)
+        tile_dma_segment<D>(Qs, seg, lane, [&](int r) {
+          return qb + min<int64_t>(i0 + r, last) * q_rs;
+        });
+      else
+        tile_dma_segment<D>(dOs, seg - C::Q_SEGS, lane, [&](int r) {
+          return db_ + min<int64_t>(i0 + r, last) * q_rs;
+        });
     }
-    if (tid < 2 * C::BQ) {
-      const int64_t row = i0 + (tid % C::BQ);
-      const int64_t li = (b * a.hq + h) * a.len_q + row;
-      if (tid < C::BQ) sreg = row < a.len_q ? lse2_of(a.lse[li]) : INFINITY;
-      else sreg = row < a.len_q ? a.delta[li] : 0.f;
-    }
-  };
-  auto sstore = [&]() {
-#pragma unroll
-    for (int i = 0; i < C::QCPT; ++i) {
-      const int c = tid + i * C::NT;
-      const int r = c / (D / 8), dc = c % (D / 8);
-      tile_store16<D>(Qs, r, dc, qreg[i]);
-      tile_store16<D>(dOs, r, dc, dreg[i]);
-    }
-    if (tid < C::BQ) lse2s[tid] = sreg;
-    else if (tid < 2 * C::BQ) dls[tid - C::BQ] = sreg;
   };
 
-  gload(0);
-  sstore();
+  stage_q(0, 0);
+  wait_vmem();
   __syncthreads();
 
 #pragma unroll 1
   for (int it = 0; it < steps; ++it) {
-    if (it + 1 < steps) gload(it + 1);
-    const int64_t r0 = int64_t(qt0 + it % nq) * C::BQ;
+    if (it + 1 < steps) stage_q(it + 1, (it + 1) & 1);  // lands while this step computes
+    const lds_u16* Qs = stage_ptr(it & 1);
+    const lds_u16* dOs = Qs + C::Q_TILE;
+    const int h = g * a.group + it / nq;
+    const int64_t r0 = int64_t(qt0 + it % nq) * C::BQ;  // first row of this step
     bool any = wave_active;
-    if (any && a.causal) any = a.q_start + min(r0 + C::BQ, a.len_q) - 1 >= a.kv_start + wk_lo;
+    if constexpr (!FULL) {
+      if (any && a.causal) any = a.q_start + min(r0 + C::BQ, a.len_q) - 1 >= a.kv_start + wk_lo;
+    }
     if (any) {
-      const bool need_mask = (a.causal && a.q_start + r0 < a.kv_start + wk_hi - 1) ||
-                             (r0 + C::BQ > a.len_q) || (wk_lo + 32 > a.len_kv);
+      // LSE (base 2) and delta of this lane's 16 rows: rows 8*(r/4) + 4*hi + r%4
+      f32x4 lx[4], dx[4];
+      {
+        const int64_t lbase = (b * a.hq + h) * a.len_q + r0;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int64_t rr = r0 + 8 * r4 + 4 * hi;
+          if (rr + 3 < a.len_q) {
+            lx[r4] = *reinterpret_cast<const f32x4*>(a.lse + lbase + 8 * r4 + 4 * hi);
+            dx[r4] = *reinterpret_cast<const f32x4*>(a.delta + lbase + 8 * r4 + 4 * hi);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const bool ok = rr + e < a.len_q;
+              lx[r4][e] = ok ? a.lse[lbase + 8 * r4 + 4 * hi + e] : -INFINITY;
+              dx[r4][e] = ok ? a.delta[lbase + 8 * r4 + 4 * hi + e] : 0.f;
+            }
+          }
+        }
+      }
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int st = 0; st < D / 16; ++st) {
         s = mfma32(tile_row8<D>(Qs, l32, 2 * st + hi), tile_row8<D>(Ks, wave * 32 + l32, 2 * st + hi), s);
         dp = mfma32(tile_row8<D>(dOs, l32, 2 * st + hi), tile_row8<D>(Vs, wave * 32 + l32, 2 * st + hi), dp);
       }
-      const int64_t rmin = a.causal ? a.kv_start + key - a.q_start - r0 : INT64_MIN / 2;
-      const int64_t rmax = a.len_q - 1 - r0;
-      const bool key_ok = key < a.len_kv;
+      bool need_mask = false;
+      if constexpr (!FULL)
+        need_mask = (a.causal && a.q_start + r0 < a.kv_start + wk_hi - 1) ||
+                    (r0 + C::BQ > a.len_q) || (wk_lo + 32 > a.len_kv);
       if (need_mask) {  // hidden scores -> -inf, so P = exp2(-inf) = 0 (c > 0)
+        const int64_t rmin = a.causal ? a.kv_start + key - a.q_start - r0 : INT64_MIN / 2;
+        const int64_t rmax = a.len_q - 1 - r0;
+        const bool key_ok = key < a.len_kv;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int ri = 8 * (r >> 2) + 4 * hi + (r & 3);
@@ -409,18 +215,15 @@ void dkdv_lds_bf16_kernel(BwdArgs a) {
         }
       }
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 x = *(const DFA_LDS f32x4*)(lse2s + 8 * r4 + 4 * hi);
-        const f32x4 y = *(const DFA_LDS f32x4*)(dls + 8 * r4 + 4 * hi);
+      for (int r4 = 0; r4 < 4; ++r4)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * r4 + e;
-          const float p = exp2_fast(fmaf(s[r], a.c, -x[e]));
+          const float p = exp2_fast(fmaf(s[r], a.c, -lse2_of(lx[r4][e])));
           s[r] = p;
-          dp[r] = p * (dp[r] - y[e]);
+          dp[r] = p * (dp[r] - dx[r4][e]);
         }
-      }
-#pragma unroll 1
+#pragma unroll
       for (int j = 0; j < 2; ++j) {
         bf16x8 pb, sb;
 #pragma unroll
@@ -432,16 +235,14 @@ void dkdv_lds_bf16_kernel(BwdArgs a) {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
           const int c0 = 32 * db + 16 * half16;
-          const bf16x8 ta =
-              cat4(tile_tr4<D>(dOs, t0, c0, lane), tile_tr4<D>(dOs, t0 + 8, c0, lane));
+          const bf16x8 ta = cat4(tile_tr4<D>(dOs, t0, c0, lane), tile_tr4<D>(dOs, t0 + 8, c0, lane));
           dv_acc[db] = mfma32(ta, pb, dv_acc[db]);
           const bf16x8 ua = cat4(tile_tr4<D>(Qs, t0, c0, lane), tile_tr4<D>(Qs, t0 + 8, c0, lane));
           dk_acc[db] = mfma32(ua, sb, dk_acc[db]);
         }
       }
     }
-    __syncthreads();
-    if (it + 1 < steps) sstore();
+    wait_vmem();  // the next step's segments this wave staged have landed
     __syncthreads();
   }
 
@@ -470,19 +271,16 @@ template <int D, int NW, int HPW, int BN>
 struct DqCfg {
   static constexpr int NT = NW * 64;
   static constexpr int BM = 32 * (NW / HPW);
-  static constexpr int CH = BN * D / 8;
-  static constexpr int CPT = CH / NT;
-  static constexpr int STAGE = 2 * BN * D;  // K tile + V tile (elements)
+  static constexpr int NSB = BN / 32;
+  static constexpr int TILE = BN * D;
+  static constexpr int SEGS = TILE / 512;
+  static constexpr int STAGE = 2 * TILE;  // K tile + V tile (elements)
   static constexpr int LDS_BYTES = 2 * STAGE * 2;
-  static_assert(CH % NT == 0, "key tile chunks must divide evenly");
+  static_assert(SEGS % NW == 0, "key tile segments must divide over the waves");
 };
 
-#ifndef DFA_DQ_OCC
-#define DFA_DQ_OCC 2  // waves per SIMD the register budget is sized for
-#endif
-
-template <int D, int NW, int HPW, int BN>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DFA_DQ_OCC, DFA_DQ_OCC)))
+template <int D, int NW, int HPW, int BN, bool FULL>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DFA_BWD_OCC, DFA_BWD_OCC)))
 void dq_bf16_kernel(BwdArgs a) {
   using C = DqCfg<D, NW, HPW, BN>;
   extern __shared__ __align__(16) uint16_t smem_generic[];
@@ -517,13 +315,8 @@ void dq_bf16_kernel(BwdArgs a) {
     const int64_t off = (b * a.len_q + row) * q_rs + int64_t(h) * D;
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
-      if (row < a.len_q) {
-        qf[st] = ld_bf16x8(a.q + off + 16 * st + 8 * hi);
-        df[st] = ld_bf16x8(a.d_o + off + 16 * st + 8 * hi);
-      } else {
-        qf[st] = bf16x8{};
-        df[st] = bf16x8{};
-      }
+      qf[st] = row < a.len_q ? ld_bf16x8(a.q + off + 16 * st + 8 * hi) : bf16x8{};
+      df[st] = row < a.len_q ? ld_bf16x8(a.d_o + off + 16 * st + 8 * hi) : bf16x8{};
     }
     if (row < a.len_q) {
       const int64_t li = (b * a.hq + h) * a.len_q + row;
@@ -543,94 +336,103 @@ void dq_bf16_kernel(BwdArgs a) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
 
-  uint4 kreg[C::CPT], vreg[C::CPT];
-  auto gload = [&](int kt) {
+  auto stage_tile = [&](int kt, int stage) {
+    lds_u16* Ks = smem + stage * C::STAGE;
+    lds_u16* Vs = Ks + C::TILE;
+    const int64_t key0 = int64_t(kt) * BN;
+    const int64_t last = a.len_kv - 1;  // rows past the chunk re-read its last key (masked)
 #pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int c = tid + i * C::NT;
-      const int key = c / (D / 8), dc = c % (D / 8);
-      const int64_t kk = int64_t(kt) * BN + key;
-      if (kk < a.len_kv) {
-        kreg[i] = ld_u4(kbase + kk * kv_rs + 8 * dc);
-        vreg[i] = ld_u4(vbase + kk * kv_rs + 8 * dc);
-      } else {
-        kreg[i] = make_uint4(0, 0, 0, 0);
-        vreg[i] = make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < C::SEGS / NW; ++i) {
+      const int seg = wave * (C::SEGS / NW) + i;
+      tile_dma_segment<D>(Ks, seg, lane, [&](int r) {
+        return kbase + min<int64_t>(key0 + r, last) * kv_rs;
+      });
+      tile_dma_segment<D>(Vs, seg, lane, [&](int r) {
+        return vbase + min<int64_t>(key0 + r, last) * kv_rs;
+      });
+    }
+  };
+  // S^T = K Q^T and dP^T = V dO^T of one 32-key sub-block (lane = query row).
+  auto sdp = [&](const lds_u16* Ks, const lds_u16* Vs, int kb, f32x16& s, f32x16& dp) {
+    s = f32x16{};
+    dp = f32x16{};
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+      s = mfma32(tile_row8<D>(Ks, kb * 32 + l32, 2 * st + hi), qf[st], s);
+      dp = mfma32(tile_row8<D>(Vs, kb * 32 + l32, 2 * st + hi), df[st], dp);
+    }
+  };
+  // dS^T = P^T (dP^T - delta) (hidden scores already -inf), dQ^T += K^T dS^T.
+  auto update = [&](const lds_u16* Ks, int kb, const f32x16& s, f32x16& dp) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = exp2_fast(fmaf(s[r], a.c, -lse2));
+      dp[r] = p * (dp[r] - dl);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      bf16x8 sb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sb[e] = static_cast<__bf16>(dp[8 * j + e]);
+      const int t0 = kb * 32 + 16 * j + 4 * hi;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int c0 = 32 * db + 16 * half16;
+        const bf16x8 ta = cat4(tile_tr4<D>(Ks, t0, c0, lane), tile_tr4<D>(Ks, t0 + 8, c0, lane));
+        acc[db] = mfma32(ta, sb, acc[db]);
       }
     }
   };
-  auto sstore = [&](int stage) {
-    lds_u16* Ks = smem + stage * C::STAGE;
-    lds_u16* Vs = Ks + BN * D;
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int c = tid + i * C::NT;
-      const int key = c / (D / 8), dc = c % (D / 8);
-      tile_store16<D>(Ks, key, dc, kreg[i]);
-      tile_store16<D>(Vs, key, dc, vreg[i]);
-    }
-  };
 
-  gload(0);
-  sstore(0);
+  stage_tile(0, 0);
+  wait_vmem();
   __syncthreads();
 
   for (int kt = 0; kt < kt_end; ++kt) {
-    if (kt + 1 < kt_end) gload(kt + 1);
+    if (kt + 1 < kt_end) stage_tile(kt + 1, (kt + 1) & 1);  // lands while this tile computes
     const lds_u16* Ks = smem + (kt & 1) * C::STAGE;
-    const lds_u16* Vs = Ks + BN * D;
+    const lds_u16* Vs = Ks + C::TILE;
     const int64_t key0 = int64_t(kt) * BN;
-    int nsb = 0;
-    if (wave_active) {
-      int64_t vis_last = a.len_kv - 1 - key0;
-      if (a.causal) vis_last = min(vis_last, a.q_start + (w_hi - 1) - a.kv_start - key0);
-      nsb = vis_last < 0 ? 0 : int(min<int64_t>(BN / 32, vis_last / 32 + 1));
-    }
-    if (nsb > 0) {
-      const bool need_mask =
-          (a.causal && a.kv_start + key0 + nsb * 32 - 1 > a.q_start + w_lo) ||
-          (key0 + nsb * 32 > a.len_kv);
-      int64_t vlim = a.len_kv - 1 - key0;
-      if (a.causal) vlim = min(vlim, a.q_start + row - a.kv_start - key0);
+    if constexpr (FULL) {
+      if (wave_active) {
+        f32x16 s, dp;
+        sdp(Ks, Vs, 0, s, dp);
+#pragma unroll 1
+        for (int kb = 0; kb < C::NSB - 1; ++kb) {
+          f32x16 s2, dp2;
+          sdp(Ks, Vs, kb + 1, s2, dp2);  // independent of the vector work below
+          update(Ks, kb, s, dp);
+          s = s2;
+          dp = dp2;
+        }
+        update(Ks, C::NSB - 1, s, dp);
+      }
+    } else {
+      int nsb = 0;
+      if (wave_active) {
+        int64_t vis_last = a.len_kv - 1 - key0;
+        if (a.causal) vis_last = min(vis_last, a.q_start + (w_hi - 1) - a.kv_start - key0);
+        nsb = vis_last < 0 ? 0 : int(min<int64_t>(C::NSB, vis_last / 32 + 1));
+      }
 #pragma unroll 1
       for (int kb = 0; kb < nsb; ++kb) {
-        {
-          f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-          for (int st = 0; st < D / 16; ++st) {
-            s = mfma32(tile_row8<D>(Ks, kb * 32 + l32, 2 * st + hi), qf[st], s);
-            dp = mfma32(tile_row8<D>(Vs, kb * 32 + l32, 2 * st + hi), df[st], dp);
-          }
-          if (need_mask) {  // hidden scores -> -inf, so P = exp2(-inf) = 0 (c > 0)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int off = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-              if (off > vlim) s[r] = -INFINITY;
-            }
-          }
+        f32x16 s, dp;
+        sdp(Ks, Vs, kb, s, dp);
+        const int64_t kfirst = key0 + kb * 32;
+        if ((a.causal && a.kv_start + kfirst + 31 > a.q_start + w_lo) || kfirst + 32 > a.len_kv) {
+          // hidden scores -> -inf, so P = exp2(-inf) = 0 (c > 0)
+          int64_t vlim = a.len_kv - 1 - kfirst;
+          if (a.causal) vlim = min(vlim, a.q_start + row - a.kv_start - kfirst);
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float p = exp2_fast(fmaf(s[r], a.c, -lse2));
-            dp[r] = p * (dp[r] - dl);
-          }
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            bf16x8 sb;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sb[e] = static_cast<__bf16>(dp[8 * j + e]);
-            const int t0 = kb * 32 + 16 * j + 4 * hi;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-              const int c0 = 32 * db + 16 * half16;
-              const bf16x8 ta =
-                  cat4(tile_tr4<D>(Ks, t0, c0, lane), tile_tr4<D>(Ks, t0 + 8, c0, lane));
-              acc[db] = mfma32(ta, sb, acc[db]);
-            }
+            const int off = 8 * (r >> 2) + 4 * hi + (r & 3);
+            if (off > vlim) s[r] = -INFINITY;
           }
         }
+        update(Ks, kb, s, dp);
       }
     }
-    if (kt + 1 < kt_end) sstore((kt + 1) & 1);
+    wait_vmem();  // the next tile's segments this wave staged have landed
     __syncthreads();
   }
 
@@ -648,65 +450,65 @@ void dq_bf16_kernel(BwdArgs a) {
     }
 }
 
-struct Plan {
-  int nw, hpw;
-};
-Plan dq_plan(int group) {
-  if (group % 4 == 0) return {4, 4};
-  if (group % 2 == 0) return {4, 2};
-  return {4, 1};
+#ifndef DFA_DQ_BN
+#define DFA_DQ_BN 64
+#endif
+constexpr int kDqBN = DFA_DQ_BN;
+constexpr int kDkvNW = 8;
+
+int dq_hpw(int group) {
+  if (group % 8 == 0) return 8;
+  if (group % 4 == 0) return 4;
+  if (group % 2 == 0) return 2;
+  return 1;
 }
-constexpr int kDqBN = 64;
-constexpr int kDkvNW = 4;
-constexpr int kDkvBQ = 64;
 
-
-template <int D, int NW, int HPW>
+template <int D, int HPW>
 dfa_status launch_dq(const dfa_attn_desc& d, BwdArgs a, hipStream_t s) {
+  constexpr int NW = 8;
   using C = DqCfg<D, NW, HPW, kDqBN>;
   a.n_tiles = int(cdiv(d.len_q, C::BM));
   a.n_hgroups = d.heads_q / HPW;
   a.n_ktiles = int(cdiv(d.len_kv, kDqBN));
-  auto kern = dq_bf16_kernel<D, NW, HPW, kDqBN>;
-  const dfa_status st = allow_lds(kern, C::LDS_BYTES, "dq_bf16_kernel");
-  if (st != DFA_OK) return st;
   dim3 grid(unsigned(a.n_tiles) * unsigned(a.n_hgroups), unsigned(d.batch));
-  hipLaunchKernelGGL(kern, grid, dim3(C::NT), C::LDS_BYTES, s, a);
-  return check_launch("dq_bf16_kernel");
+  auto go = [&](auto kern) {
+    const dfa_status st = allow_lds(kern, C::LDS_BYTES, "dq_bf16_kernel");
+    if (st != DFA_OK) return st;
+    hipLaunchKernelGGL(kern, grid, dim3(C::NT), C::LDS_BYTES, s, a);
+    return check_launch("dq_bf16_kernel");
+  };
+  if (pair_is_full(d, kDqBN)) return go(dq_bf16_kernel<D, NW, HPW, kDqBN, true>);
+  return go(dq_bf16_kernel<D, NW, HPW, kDqBN, false>);
 }
 
-#ifndef DFA_DKDV_KV_LDS
-#define DFA_DKDV_KV_LDS 1  // K, V in LDS, two waves per SIMD
-#endif
+template <int D>
+dfa_status launch_dkdv(const dfa_attn_desc& d, BwdArgs a, hipStream_t s) {
+  using C = DkvCfg<D, kDkvNW>;
+  dim3 grid(unsigned(cdiv(d.len_kv, C::BK)) * unsigned(d.heads_kv), unsigned(d.batch));
+  auto go = [&](auto kern) {
+    const dfa_status st = allow_lds(kern, C::LDS_BYTES, "dkdv_bf16_kernel");
+    if (st != DFA_OK) return st;
+    hipLaunchKernelGGL(kern, grid, dim3(C::NT), C::LDS_BYTES, s, a);
+    return check_launch("dkdv_bf16_kernel");
+  };
+  if (pair_is_full(d, C::BK) && d.len_q % C::BQ == 0)
+    return go(dkdv_bf16_kernel<D, kDkvNW, true>);
+  return go(dkdv_bf16_kernel<D, kDkvNW, false>);
+}
 
 template <int D>
 dfa_status launch_bwd_d(const dfa_attn_desc& d, BwdArgs a, hipStream_t s, int parts) {
-  using KC = DkvCfg<D, kDkvNW, kDkvBQ>;
-  if (!(parts & 1)) {
-    // dQ only
-  } else if constexpr (DFA_DKDV_KV_LDS && D == 128) {
-    using LC = DkvLdsCfg<D, 8>;
-    auto kern = dkdv_lds_bf16_kernel<D, 8>;
-    const dfa_status st = allow_lds(kern, LC::LDS_BYTES, "dkdv_lds_bf16_kernel");
+  if (parts & 1) {
+    const dfa_status st = launch_dkdv<D>(d, a, s);
     if (st != DFA_OK) return st;
-    dim3 grid(unsigned(cdiv(d.len_kv, LC::BK)) * unsigned(d.heads_kv), unsigned(d.batch));
-    hipLaunchKernelGGL(kern, grid, dim3(LC::NT), LC::LDS_BYTES, s, a);
-    const dfa_status st2 = check_launch("dkdv_lds_bf16_kernel");
-    if (st2 != DFA_OK) return st2;
-  } else {
-    auto kern = dkdv_bf16_kernel<D, kDkvNW, kDkvBQ>;
-    const dfa_status st = allow_lds(kern, KC::LDS_BYTES, "dkdv_bf16_kernel");
-    if (st != DFA_OK) return st;
-    dim3 grid(unsigned(cdiv(d.len_kv, KC::BK)) * unsigned(d.heads_kv), unsigned(d.batch));
-    hipLaunchKernelGGL(kern, grid, dim3(KC::NT), KC::LDS_BYTES, s, a);
-    const dfa_status st2 = check_launch("dkdv_bf16_kernel");
-    if (st2 != DFA_OK) return st2;
   }
   if (!(parts & 2)) return DFA_OK;
-  const Plan p = dq_plan(a.group);
-  if (p.hpw == 4) return launch_dq<D, 4, 4>(d, a, s);
-  if (p.hpw == 2) return launch_dq<D, 4, 2>(d, a, s);
-  return launch_dq<D, 4, 1>(d, a, s);
+  switch (dq_hpw(a.group)) {
+    case 8: return launch_dq<D, 8>(d, a, s);
+    case 4: return launch_dq<D, 4>(d, a, s);
+    case 2: return launch_dq<D, 2>(d, a, s);
+    default: return launch_dq<D, 1>(d, a, s);
+  }
 }
 
 }  // namespace
