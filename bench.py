@@ -109,10 +109,15 @@ def cpu_baseline(w, host, worker, budget_s):
         pairs = sum(q0 + i + 1 for i in range(r))
         return dt, pairs * 14 * w.head_dim
 
+    # grow the sample until one run takes most of the budget (cost is not
+    # linear in r at small r, so a single extrapolation undershoots)
     r = 8
-    dt, _ = run(r)
-    r = int(max(8, min(c, r * budget_s / max(dt, 1e-3))))
     dt, flops = run(r)
+    for _ in range(5):
+        if dt >= 0.6 * budget_s or r >= c:
+            break
+        r = int(min(c, max(r + 8, r * min(8.0, budget_s / max(dt, 1e-3)))))
+        dt, flops = run(r)
     threads = sum(i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas")
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads or 1),
             "kind": "oracle",

@@ -158,8 +158,38 @@ void dkdv_bf16_kernel(BwdArgs a) {
     }
   };
 
+  // LSE and delta of this lane's 16 rows of step `it` (rows 8*(r/4) + 4*hi +
+  // r%4 of the step): LSE in -log2 form (P = exp2(fma(s, c, nl))), rows
+  // without keys or past the chunk give nl = -inf, so P = 0.
+  f32x4 nl[4], dl[4];
+  auto load_rows = [&](int it) {
+    const int h = g * a.group + it / nq;
+    const int64_t r0 = int64_t(qt0 + it % nq) * C::BQ;
+    const int64_t lbase = (b * a.hq + h) * a.len_q + r0;
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int64_t rr = r0 + 8 * r4 + 4 * hi;
+      f32x4 x, y;
+      if (FULL || rr + 3 < a.len_q) {
+        x = *reinterpret_cast<const f32x4*>(a.lse + lbase + 8 * r4 + 4 * hi);
+        y = *reinterpret_cast<const f32x4*>(a.delta + lbase + 8 * r4 + 4 * hi);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool ok = rr + e < a.len_q;
+          x[e] = ok ? a.lse[lbase + 8 * r4 + 4 * hi + e] : -INFINITY;
+          y[e] = ok ? a.delta[lbase + 8 * r4 + 4 * hi + e] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) nl[r4][e] = x[e] > -INFINITY ? -x[e] * kLog2e : -INFINITY;
+      dl[r4] = y;
+    }
+  };
+
   stage_q(0, 0);
   wait_vmem();
+  load_rows(0);
   __syncthreads();
 
 #pragma unroll 1
@@ -167,39 +197,21 @@ void dkdv_bf16_kernel(BwdArgs a) {
     if (it + 1 < steps) stage_q(it + 1, (it + 1) & 1);  // lands while this step computes
     const lds_u16* Qs = stage_ptr(it & 1);
     const lds_u16* dOs = Qs + C::Q_TILE;
-    const int h = g * a.group + it / nq;
     const int64_t r0 = int64_t(qt0 + it % nq) * C::BQ;  // first row of this step
     bool any = wave_active;
     if constexpr (!FULL) {
       if (any && a.causal) any = a.q_start + min(r0 + C::BQ, a.len_q) - 1 >= a.kv_start + wk_lo;
     }
     if (any) {
-      // LSE (base 2) and delta of this lane's 16 rows: rows 8*(r/4) + 4*hi + r%4
-      f32x4 lx[4], dx[4];
-      {
-        const int64_t lbase = (b * a.hq + h) * a.len_q + r0;
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int64_t rr = r0 + 8 * r4 + 4 * hi;
-          if (rr + 3 < a.len_q) {
-            lx[r4] = *reinterpret_cast<const f32x4*>(a.lse + lbase + 8 * r4 + 4 * hi);
-            dx[r4] = *reinterpret_cast<const f32x4*>(a.delta + lbase + 8 * r4 + 4 * hi);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const bool ok = rr + e < a.len_q;
-              lx[r4][e] = ok ? a.lse[lbase + 8 * r4 + 4 * hi + e] : -INFINITY;
-              dx[r4][e] = ok ? a.delta[lbase + 8 * r4 + 4 * hi + e] : 0.f;
-            }
-          }
-        }
-      }
+      // S first, then dP: the exponentials below can run while dP's
+      // instructions are still in the matrix pipe.
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int st = 0; st < D / 16; ++st) {
+      for (int st = 0; st < D / 16; ++st)
         s = mfma32(tile_row8<D>(Qs, l32, 2 * st + hi), tile_row8<D>(Ks, wave * 32 + l32, 2 * st + hi), s);
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st)
         dp = mfma32(tile_row8<D>(dOs, l32, 2 * st + hi), tile_row8<D>(Vs, wave * 32 + l32, 2 * st + hi), dp);
-      }
       bool need_mask = false;
       if constexpr (!FULL)
         need_mask = (a.causal && a.q_start + r0 < a.kv_start + wk_hi - 1) ||
@@ -214,35 +226,45 @@ void dkdv_bf16_kernel(BwdArgs a) {
           if (!key_ok || ri < rmin || ri > rmax) s[r] = -INFINITY;
         }
       }
+      // P, then dV^T += dO^T P; dS is formed while those instructions run.
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * r4 + e;
-          const float p = exp2_fast(fmaf(s[r], a.c, -lse2_of(lx[r4][e])));
-          s[r] = p;
-          dp[r] = p * (dp[r] - dx[r4][e]);
-        }
+      for (int r = 0; r < 16; ++r) s[r] = exp2_fast(fmaf(s[r], a.c, nl[r >> 2][r & 3]));
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        bf16x8 pb, sb;
+        bf16x8 pb;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pb[e] = static_cast<__bf16>(s[8 * j + e]);
-          sb[e] = static_cast<__bf16>(dp[8 * j + e]);
-        }
+        for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(s[8 * j + e]);
         const int t0 = 16 * j + 4 * hi;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
           const int c0 = 32 * db + 16 * half16;
           const bf16x8 ta = cat4(tile_tr4<D>(dOs, t0, c0, lane), tile_tr4<D>(dOs, t0 + 8, c0, lane));
           dv_acc[db] = mfma32(ta, pb, dv_acc[db]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dp[r] = s[r] * (dp[r] - dl[r >> 2][r & 3]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        bf16x8 sb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sb[e] = static_cast<__bf16>(dp[8 * j + e]);
+        const int t0 = 16 * j + 4 * hi;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const int c0 = 32 * db + 16 * half16;
           const bf16x8 ua = cat4(tile_tr4<D>(Qs, t0, c0, lane), tile_tr4<D>(Qs, t0 + 8, c0, lane));
           dk_acc[db] = mfma32(ua, sb, dk_acc[db]);
         }
       }
     }
-    wait_vmem();  // the next step's segments this wave staged have landed
+    // The next stage this wave staged must land before the barrier; the next
+    // step's LSE / delta rows are issued after that wait, so their latency
+    // hides behind the barrier and the next S / dP.
+    if (it + 1 < steps) {
+      wait_vmem();
+      load_rows(it + 1);
+    }
     __syncthreads();
   }
 

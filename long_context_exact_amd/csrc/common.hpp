@@ -30,6 +30,14 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// 16x16x32 bf16 matrix FMA, fp32 accumulate (one wave):
+//   A[i][k]: i = l % 16, k = 8 * (l / 16) + e
+//   B[k][j]: j = l % 16, k = 8 * (l / 16) + e
+//   C[i][j] element r (0..3): j = l % 16, i = 4 * (l / 16) + r
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Value of `x` held by lane (l ^ 32) of the wave.
@@ -49,21 +57,24 @@ __device__ __forceinline__ bf16x8 cat4(bf16x4 a, bf16x4 b) {
 
 // ---- row-major bf16 tiles in LDS ------------------------------------------
 // A tile holds rows of D bf16 (no padding).  gfx950's LDS serves 256 bytes
-// (64 four-byte banks) per cycle, so its 16-byte chunks are XOR-swizzled per
-// row such that
-//  * a 16-byte fragment read of one chunk by 16 consecutive rows (16 lanes),
-//  * a transpose read (below) of 4 consecutive rows x 4 adjacent chunks
-//    (32 lanes), and
-//  * a 16-byte store of 16 consecutive chunks of one row
-// each touch 16 distinct 16-byte slots of a 256-byte bank line.
-//   D = 128 (16 chunks, one row per line):  chunk c of row r at c ^ g,
-//     g = 4 * (r % 4) + (r / 4) % 4;
-//   D = 64 (8 chunks, two rows per line):   g = 4 * ((r / 2) % 2) + (r / 4) % 4.
+// (64 four-byte banks) per cycle; a ds_read_b128 takes four cycles, each
+// serving the 16 lanes that agree in lane bit 5 and in the parity of lane
+// bits 2..4 (measured with the bank-conflict counter).  The 16-byte chunks
+// are XOR-swizzled per row such that each of these touches 16 distinct
+// 16-byte slots of a 256-byte bank line:
+//  * a 16-byte fragment read of one chunk where lane l reads row l % 32
+//    (each cycle then holds 16 rows that differ mod 16),
+//  * a 32x32-operand transpose read: 4 consecutive rows x 4 adjacent chunks,
+//  * a 16x16-operand transpose read: 8 consecutive rows x 2 adjacent chunks,
+//  * a 16-byte store of 16 consecutive chunks (one row, or two of D = 64).
+// Chunk c of row r sits at c ^ g(r) with
+//   D = 128: g = 4 * (r % 4) + 2 * ((r / 4) % 2) + (r / 8) % 2,
+//   D = 64:  g = 4 * ((r / 2) % 2) + 2 * ((r / 4) % 2) + (r / 8) % 2.
 template <int D>
 __device__ __forceinline__ int swz(int row, int chunk) {
   static_assert(D == 64 || D == 128, "tile rows of 64 or 128 elements");
-  const int g = D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3))
-                         : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+  const int lo = (((row >> 2) & 1) << 1) | ((row >> 3) & 1);
+  const int g = D == 128 ? (((row & 3) << 2) | lo) : ((((row >> 1) & 1) << 2) | lo);
   return row * D + ((chunk ^ g) << 3);
 }
 
