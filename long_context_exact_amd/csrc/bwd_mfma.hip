@@ -144,6 +144,17 @@ void dkdv_bf16_kernel(BwdArgs a) {
     const uint16_t* db_ = a.d_o + b * a.len_q * q_rs + int64_t(h) * D;
     lds_u16* Qs = stage_ptr(stage);
     lds_u16* dOs = Qs + C::Q_TILE;
+    if constexpr (FULL) {  // every row of every step is in range
+      constexpr int RPS = 512 / D;
+      for (int seg = wave; seg < 2 * C::Q_SEGS; seg += NW) {
+        if (seg < C::Q_SEGS)
+          tile_dma_segment_rows<D>(Qs, seg, lane, qb + (i0 + seg * RPS) * q_rs, uint32_t(q_rs * 2));
+        else
+          tile_dma_segment_rows<D>(dOs, seg - C::Q_SEGS, lane,
+                                   db_ + (i0 + (seg - C::Q_SEGS) * RPS) * q_rs, uint32_t(q_rs * 2));
+      }
+      return;
+    }
     const int64_t last = a.len_q - 1;  // rows past the chunk re-read its last row (P = 0)
     // 2 * Q_SEGS segments (Q then dO) spread over the waves
     for (int seg = wave; seg < 2 * C::Q_SEGS; seg += NW) {
@@ -362,6 +373,17 @@ void dq_bf16_kernel(BwdArgs a) {
     lds_u16* Ks = smem + stage * C::STAGE;
     lds_u16* Vs = Ks + C::TILE;
     const int64_t key0 = int64_t(kt) * BN;
+    if constexpr (FULL) {  // every row of every tile is in range
+      constexpr int RPS = 512 / D;
+#pragma unroll
+      for (int i = 0; i < C::SEGS / NW; ++i) {
+        const int seg = wave * (C::SEGS / NW) + i;
+        const int64_t r0 = (key0 + seg * RPS) * kv_rs;
+        tile_dma_segment_rows<D>(Ks, seg, lane, kbase + r0, uint32_t(kv_rs * 2));
+        tile_dma_segment_rows<D>(Vs, seg, lane, vbase + r0, uint32_t(kv_rs * 2));
+      }
+      return;
+    }
     const int64_t last = a.len_kv - 1;  // rows past the chunk re-read its last key (masked)
 #pragma unroll
     for (int i = 0; i < C::SEGS / NW; ++i) {

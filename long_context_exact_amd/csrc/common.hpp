@@ -135,6 +135,23 @@ __device__ __forceinline__ void tile_dma_segment(lds_u16* tile, int seg, int lan
   __builtin_amdgcn_global_load_lds(src, (lds_void*)(tile + seg * 512), 16, 0, 0);
 }
 
+// Same staging when the segment's rows are consecutive rows of one tensor,
+// all in range: `seg_base` (wave-uniform) is the segment's first row and
+// rows are `row_bytes` apart, so each lane adds only a 32-bit offset.
+template <int D>
+__device__ __forceinline__ void tile_dma_segment_rows(lds_u16* tile, int seg, int lane,
+                                                      const uint16_t* seg_base, uint32_t row_bytes) {
+  constexpr int ROWS_PER_SEG = 512 / D;
+  constexpr int CHUNKS = D / 8;
+  const int r_in = lane / CHUNKS;
+  const int row = seg * ROWS_PER_SEG + r_in;
+  const int logical = (swz<D>(row, lane % CHUNKS) - row * D) >> 3;
+  const uint32_t off = uint32_t(r_in) * row_bytes + uint32_t(logical) * 16u;
+  typedef DFA_LDS void lds_void;
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(seg_base) + off,
+                                   (lds_void*)(tile + seg * 512), 16, 0, 0);
+}
+
 // Wait for this wave's outstanding global loads (including LDS-direct ones).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 

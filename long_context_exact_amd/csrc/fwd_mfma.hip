@@ -121,6 +121,17 @@ void fwd_bf16_kernel(FwdArgs a) {
     lds_u16* Ks = smem + stage * C::STAGE;
     lds_u16* Vs = Ks + C::TILE;
     const int64_t key0 = int64_t(kt) * BN;
+    if constexpr (FULL) {  // every row of every tile is in range
+      constexpr int RPS = 512 / D;
+#pragma unroll
+      for (int i = 0; i < C::SEGS / NW; ++i) {
+        const int seg = wave * (C::SEGS / NW) + i;
+        const int64_t r0 = (key0 + seg * RPS) * kv_rs;
+        tile_dma_segment_rows<D>(Ks, seg, lane, kbase + r0, uint32_t(kv_rs * 2));
+        tile_dma_segment_rows<D>(Vs, seg, lane, vbase + r0, uint32_t(kv_rs * 2));
+      }
+      return;
+    }
     const int64_t last = a.len_kv - 1;  // rows past the chunk re-read its last key (masked)
 #pragma unroll
     for (int i = 0; i < C::SEGS / NW; ++i) {
