@@ -36,6 +36,8 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # MI355X dense MFMA peaks
 
 # Profiler names of the kernels the default build launches for bf16 head_dim 128.
 KERNEL_NAMES = {"fwd": "fwd_bf16_kernel", "dkdv": "dkdv_bf16_kernel", "dq": "dq_bf16_kernel"}
+# fp32 inputs run the exact fp32 kernels (one wave per row, vector ALU, no MFMA)
+KERNEL_NAMES_F32 = {"fwd": "fwd_f32_kernel", "dkdv": "dkdv_f32_kernel", "dq": "dq_f32_kernel"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = {"fwd_bf16_kernel": "fwd_mfma.hip", "dkdv_bf16_kernel": "bwd_mfma.hip",
                   "dq_bf16_kernel": "bwd_mfma.hip"}
@@ -104,26 +106,31 @@ def cpu_baseline(w, host, worker, budget_s):
         q0 = a * c + c - r
         t0 = time.perf_counter()
         o, lse = oracle.attention_fwd(q, kpre, vpre, w.scale, True, q0, 0)
+        t1 = time.perf_counter()
         oracle.attention_bwd(q, kpre, vpre, o, lse, do, w.scale, True, q0, 0)
-        dt = time.perf_counter() - t0
+        t2 = time.perf_counter()
         pairs = sum(q0 + i + 1 for i in range(r))
-        return dt, pairs * 14 * w.head_dim
+        return t2 - t0, pairs * 14 * w.head_dim, (t1 - t0, pairs * 4 * w.head_dim), \
+            (t2 - t1, pairs * 10 * w.head_dim)
 
     # grow the sample until one run takes most of the budget (cost is not
     # linear in r at small r, so a single extrapolation undershoots)
     r = 8
-    dt, flops = run(r)
+    dt, flops, fw, bw = run(r)
     for _ in range(5):
         if dt >= 0.6 * budget_s or r >= c:
             break
         r = int(min(c, max(r + 8, r * min(8.0, budget_s / max(dt, 1e-3)))))
-        dt, flops = run(r)
-    threads = sum(i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas")
+        dt, flops, fw, bw = run(r)
+    blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    threads = sum(i.get("num_threads", 0) for i in blas)
+    lib = ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in blas) or "unknown"
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads or 1),
             "kind": "oracle",
-            "sample": f"float64 numpy oracle, fwd+bwd of the last {r} query rows of chunk {a}, "
-                      f"query head 0, over their full causal prefix ({a * c + c} keys); "
-                      f"{dt:.1f} s, {flops:.3e} algorithmic FLOP"}
+            "sample": f"float64 numpy oracle ({lib}), fwd+bwd of the last {r} query rows of chunk "
+                      f"{a}, query head 0, over their full causal prefix ({a * c + c} keys); "
+                      f"{dt:.1f} s, {flops:.3e} algorithmic FLOP",
+            "fwd_gflops": round(fw[1] / fw[0] / 1e9, 2), "bwd_gflops": round(bw[1] / bw[0] / 1e9, 2)}
 
 
 def copy_calibration(gib: float):
@@ -140,8 +147,8 @@ def copy_calibration(gib: float):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gqa64x8_512k_w15")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -220,15 +227,18 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     wall0 = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
+    evs[0].record()
+    for i in range(args.steps):
         step()
-    ev1.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    step_ms = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    median_ms = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else \
+        0.5 * (step_ms[len(step_ms) // 2 - 1] + step_ms[len(step_ms) // 2])
     tflops = flop / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
 
@@ -259,16 +269,17 @@ def main():
     pairs_x_heads = sum(pairs_of(it[4], w.chunk) for it in timed) * w.batch * w.heads_q
     # name in the profiler, time per step, flop per step (the kernel's own
     # contractions on unmasked pairs: forward 2 = 4d, dK/dV 4 = 8d, dQ 3 = 6d)
-    kernels = {KERNEL_NAMES["fwd"]: (per_call(fwd_call, timed), pairs_x_heads * 4 * w.head_dim)}
+    names = KERNEL_NAMES if w.dtype == "bf16" else KERNEL_NAMES_F32
+    kernels = {names["fwd"]: (per_call(fwd_call, timed), pairs_x_heads * 4 * w.head_dim)}
     if w.backward:
-        kernels[KERNEL_NAMES["dkdv"]] = (per_call(bwd_call(1), timed),
+        kernels[names["dkdv"]] = (per_call(bwd_call(1), timed),
                                          pairs_x_heads * 8 * w.head_dim)
-        kernels[KERNEL_NAMES["dq"]] = (per_call(bwd_call(2), timed),
+        kernels[names["dq"]] = (per_call(bwd_call(2), timed),
                                        pairs_x_heads * 6 * w.head_dim)
     nl = len(timed)
     name, (kms, kflop) = max(kernels.items(), key=lambda kv: kv[1][0])
     achieved = kflop / (kms * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": name, "achieved": round(achieved, 2), "peak": peak,
+    roofline = {"bound": "mfma" if w.dtype == "bf16" else "alu", "kernel": name, "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": traffic_of(name, nl), "avg_launch_ms": round(kms / nl, 3),
                 "launches_per_step": nl, "flop_per_launch": kflop / nl,
@@ -282,6 +293,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "pct_of_peak": round(100 * tflops / peak, 2),
+        "median_ms_per_step": round(median_ms, 3),
+        "median_value": round(flop / (median_ms * 1e-3) / 1e12, 2),
         "config": {"workload": w.name, "chunk": w.chunk, "workers": w.workers,
                    "total_seq": w.total_len, "heads_q": w.heads_q, "heads_kv": w.heads_kv,
                    "head_dim": w.head_dim, "batch": w.batch,
