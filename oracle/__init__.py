@@ -13,9 +13,10 @@ paper's section / figure / appendix as that page tags them.
 
 Modules
 -------
-attention  exact causal softmax attention (forward, LSE merge, backward)
-schedule   the chunk-pair schedules (unbalanced and load-balanced) and the
-           causal tile map of one chunk pair
+attention  exact causal softmax attention (forward, LSE merge, backward),
+           optionally restricted to a local sliding window
+schedule   the chunk-pair schedules (unbalanced, load-balanced and
+           sliding-window) and the causal tile map of one chunk pair
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against facts the
 oracle does not compute itself (brute force, closed forms, invariants,
@@ -32,5 +33,6 @@ from .attention import (  # noqa: F401
 from .schedule import (  # noqa: F401
     balanced_schedule,
     unbalanced_schedule,
+    window_schedule,
     causal_tile_map,
 )

@@ -23,19 +23,29 @@ It reproduces the paper's theoretical speedups over one device at P = 8
 tends to zero for even P (§3.2), the doubling over the unbalanced version
 (§1) and a forward traffic of N*d elements per worker (App. D).
 
+Local sliding window ([DistFlashAttn App. F, discussion of sparse
+attention]): when a query sees only the W tokens ending at itself, the work
+is already nearly even across workers, so each worker keeps its own query
+chunk and only shortens the loop of the unbalanced schedule to the key/value
+chunks that hold keys inside some window of its queries (with W <= C worker
+7 of 8 visits chunks 6 and 7 only).  No helpers, no rebalancing.
+
 Items are tuples (step, worker, q_chunk, kv_chunk, kind, owner), sorted by
-(step, worker); kind 0 = diagonal (causal mask), 1 = full; owner = q_chunk.
+(step, worker); kind 0 = diagonal (causal mask), 1 = full, 2 = band (an
+off-diagonal pair that a sliding window cuts: some pairs of it hidden);
+owner = q_chunk.
 """
 
 from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["balanced_schedule", "unbalanced_schedule", "causal_tile_map",
-           "DIAG", "FULL"]
+__all__ = ["balanced_schedule", "unbalanced_schedule", "window_schedule",
+           "causal_tile_map", "DIAG", "FULL", "BAND"]
 
 DIAG = 0
 FULL = 1
+BAND = 2
 
 
 def unbalanced_schedule(num_workers: int):
@@ -70,8 +80,27 @@ def balanced_schedule(num_workers: int):
     return items, steps
 
 
+def window_schedule(num_workers: int, chunk_len: int, window: int):
+    """(items, num_steps) of the sliding-window schedule: worker w does
+    (w, w - t) at step t for every t whose chunk pair holds a pair of
+    tokens less than `window` apart (the closest such pair is (t - 1) * C + 1
+    positions apart for t >= 1); kind FULL when even the farthest pair,
+    (t + 1) * C - 1 apart, is inside the window, else BAND."""
+    p, c, w_ = int(num_workers), int(chunk_len), int(window)
+    if p < 1 or c < 1 or w_ < 1:
+        raise ValueError("num_workers, chunk_len and window must be >= 1")
+    items = []
+    t = 0
+    while t < p and (t == 0 or (t - 1) * c + 1 < w_):
+        kind = DIAG if t == 0 else (FULL if (t + 1) * c - 1 < w_ else BAND)
+        for w in range(t, p):
+            items.append((t, w, w, w - t, kind, w))
+        t += 1
+    return items, t
+
+
 def causal_tile_map(len_q: int, len_k: int, q_start: int, kv_start: int,
-                    causal: bool, bm: int, bn: int) -> np.ndarray:
+                    causal: bool, bm: int, bn: int, window: int = 0) -> np.ndarray:
     """Which (query tile, key tile) pairs of one chunk pair carry visible
     scores, and which of them straddle the causal diagonal.
 
@@ -81,7 +110,10 @@ def causal_tile_map(len_q: int, len_k: int, q_start: int, kv_start: int,
         kv_start + kt*bn <= q_start + min((qt+1)*bm, len_q) - 1,
     and needs the element mask iff, in addition, its last key is after its
     first query.  Skipping the other tiles is how causal attention avoids the
-    doubled work the paper attributes to Ring Attention (§2).
+    doubled work the paper attributes to Ring Attention (§2).  With a sliding
+    window of W tokens a tile is also skipped when its last key is W or more
+    positions behind its first query, and masked when its first key is W or
+    more positions behind its last query (App. F).
 
     Returns uint8 [ceil(len_q/bm), ceil(len_k/bn)]: 0 skipped, 1 visited
     unmasked, 2 visited with the element mask.
@@ -97,6 +129,7 @@ def causal_tile_map(len_q: int, len_k: int, q_start: int, kv_start: int,
             last_k = kv_start + min((kt + 1) * bn, len_k) - 1
             if not causal:
                 out[qt, kt] = 1
-            elif first_k <= last_q:
-                out[qt, kt] = 2 if last_k > first_q else 1
+            elif first_k <= last_q and (window <= 0 or first_q - last_k < window):
+                masked = last_k > first_q or (window > 0 and last_q - first_k >= window)
+                out[qt, kt] = 2 if masked else 1
     return out
