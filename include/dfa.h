@@ -29,8 +29,8 @@
  * Errors: arguments are checked before anything is enqueued; on a non-OK
  * status nothing was enqueued (except DFA_ERR_HIP, where a launch failed)
  * and dfa_last_error() holds a message.  No C++ exception crosses the ABI.
- * dfa_balanced_schedule and all argument checks never touch the HIP
- * runtime, so they work on a machine without a GPU.
+ * The schedules and all argument checks never touch the HIP runtime, so
+ * they work on a machine without a GPU.
  *
  * Thread safety: every call is stateless and may be made from any thread.
  */
@@ -55,8 +55,9 @@ typedef enum { DFA_F32 = 0, DFA_BF16 = 1 } dfa_dtype;
 
 /* One chunk pair of a schedule.  kind: 0 = diagonal pair (q_chunk ==
  * kv_chunk, needs the causal element mask), 1 = full pair (q_chunk >
- * kv_chunk, every score visible).  owner = q_chunk: the worker whose query
- * rows these are; owner != worker marks a helper item. */
+ * kv_chunk, every score visible), 2 = band pair (q_chunk > kv_chunk, a
+ * sliding window hides part of it).  owner = q_chunk: the worker whose
+ * query rows these are; owner != worker marks a helper item. */
 typedef struct {
   int32_t step, worker, q_chunk, kv_chunk, kind, owner;
 } dfa_work_item;
@@ -75,6 +76,11 @@ typedef struct {
                                kv_start + j <= q_start + i; 0: all visible */
   float scale;          /* score scale sigma (1/sqrt(head_dim)), finite    */
   dfa_dtype dtype;      /* element type of Q, K, V, O (final) and dO       */
+  int64_t window;       /* 0: no window.  > 0 (needs causal = 1): local
+                           sliding window, key j visible to query i only if
+                           (q_start + i) - (kv_start + j) < window, i.e. a
+                           query sees itself and the window - 1 tokens
+                           before it ([DistFlashAttn App. F])             */
 } dfa_attn_desc;
 
 /* Chunk-pair schedule of P = num_workers workers over P contiguous chunks
@@ -94,13 +100,30 @@ dfa_status dfa_balanced_schedule(int32_t num_workers, int32_t balanced,
                                  dfa_work_item* items, int64_t capacity,
                                  int64_t* num_items, int32_t* num_steps);
 
+/* Chunk-pair schedule of the local sliding window ([DistFlashAttn App. F]:
+ * with a window the work is already nearly even, so each worker keeps its
+ * own query chunk and shortens its loop to the key/value chunks that hold
+ * keys inside some window of its queries; with window <= chunk_len worker
+ * 7 of 8 visits chunks 6 and 7 only).  Worker w does (w, w - t) at step t
+ * for every t with (t - 1) * chunk_len + 1 < window (t = 0 always); kind 1
+ * when (t + 1) * chunk_len - 1 < window, else 2.  No helper items.  Items
+ * sorted by (step, worker); array, capacity and counts as in
+ * dfa_balanced_schedule.  num_workers in [1, 65536]; chunk_len and window
+ * >= 1. */
+dfa_status dfa_window_schedule(int32_t num_workers, int64_t chunk_len,
+                               int64_t window, dfa_work_item* items,
+                               int64_t capacity, int64_t* num_items,
+                               int32_t* num_steps);
+
 /* Partial attention of one chunk pair: the normalised output and its LSE
  * ([DistFlashAttn App. D]: the forward returns output and logsumexp values;
  * §3.2: partial outputs and softmax statistics are what a helper returns).
  *   q [B,len_q,Hq,d], k and v [B,len_kv,Hkv,d] in desc->dtype;
  *   o_part [B,len_q,Hq,d] float32 and lse [B,Hq,len_q] float32 are
  *   overwritten.  Only the causal prefix is computed: key tiles entirely
- *   after a query tile's last row are skipped (§2, §3.2). */
+ *   after a query tile's last row are skipped (§2, §3.2), and with a
+ *   window so are key tiles entirely outside every window of the tile's
+ *   rows (App. F). */
 dfa_status dfa_attn_fwd_partial(const dfa_attn_desc* desc, const void* q,
                                 const void* k, const void* v, float* o_part,
                                 float* lse, void* hip_stream);
@@ -158,8 +181,8 @@ dfa_status dfa_test_tile_shape(const dfa_attn_desc* desc, int32_t* bm,
 /* Runs the same forward as dfa_attn_fwd_partial and records, per batch
  * row 0 and query-head tile 0, which (query tile, key tile) pairs the
  * kernel visited: visits [ceil(len_q/bm), ceil(len_kv/bn)] uint8 DEVICE
- * array, caller-zeroed; 1 = visited without the causal element mask,
- * 2 = visited with it, 0 = skipped. */
+ * array, caller-zeroed; 1 = visited without the element mask (causal or
+ * window), 2 = visited with it, 0 = skipped. */
 dfa_status dfa_test_fwd_tile_visits(const dfa_attn_desc* desc, const void* q,
                                     const void* k, const void* v,
                                     float* o_part, float* lse,

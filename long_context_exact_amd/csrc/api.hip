@@ -29,6 +29,9 @@ dfa_status check_desc(const char* fn, const dfa_attn_desc* d) {
   if (d->len_q < 0 || d->len_kv < 0 || d->q_start < 0 || d->kv_start < 0)
     return fail(DFA_ERR_INVALID, f + ": lengths and starts must be >= 0");
   if (d->causal != 0 && d->causal != 1) return fail(DFA_ERR_INVALID, f + ": causal must be 0 or 1");
+  if (d->window < 0) return fail(DFA_ERR_INVALID, f + ": window must be >= 0");
+  if (d->window > 0 && d->causal != 1)
+    return fail(DFA_ERR_INVALID, f + ": a sliding window needs causal = 1");
   if (!std::isfinite(d->scale) || d->scale < 0.f)
     return fail(DFA_ERR_INVALID, f + ": scale must be finite and >= 0");
   if (d->dtype != DFA_F32 && d->dtype != DFA_BF16)

@@ -44,6 +44,7 @@ struct BwdArgs {
   int32_t n_tiles, n_hgroups, n_ktiles;
   float c;      // scale * log2(e), > 0
   float scale;
+  int64_t win;  // sliding window in tokens; a huge value when there is none
 };
 
 // LSE in base 2 for the exp2 form; a row without keys (LSE = -inf) gets +inf
@@ -105,12 +106,16 @@ void dkdv_bf16_kernel(BwdArgs a) {
   const int64_t q_rs = int64_t(a.hq) * D;
   const int64_t kv_rs = int64_t(a.hkv) * D;
 
-  // Query rows that see at least one key of this workgroup.
+  // Query rows that see at least one key of this workgroup: from the first
+  // row at or after its first key, to the last row whose window still
+  // reaches its last key.
   int64_t i_begin = 0;
   if (a.causal) i_begin = max<int64_t>(0, a.kv_start + k_lo - a.q_start);
-  if (i_begin >= a.len_q) return;  // uniform over the workgroup
+  const int64_t i_end =
+      min<int64_t>(a.len_q, a.kv_start + min<int64_t>(k_lo + C::BK, a.len_kv) - 1 + a.win - a.q_start);
+  if (i_begin >= i_end) return;  // uniform over the workgroup
   const int qt0 = int(i_begin / C::BQ);
-  const int nq = int(cdiv(a.len_q, C::BQ)) - qt0;
+  const int nq = int(cdiv(i_end, C::BQ)) - qt0;
   const int steps = a.group * nq;
 
   {  // the workgroup's K and V rows, once
@@ -212,6 +217,7 @@ void dkdv_bf16_kernel(BwdArgs a) {
     bool any = wave_active;
     if constexpr (!FULL) {
       if (any && a.causal) any = a.q_start + min(r0 + C::BQ, a.len_q) - 1 >= a.kv_start + wk_lo;
+      if (any) any = a.q_start + r0 - (a.kv_start + wk_hi - 1) < a.win;
     }
     if (any) {
       // S first, then dP: the exponentials below can run while dP's
@@ -226,10 +232,11 @@ void dkdv_bf16_kernel(BwdArgs a) {
       bool need_mask = false;
       if constexpr (!FULL)
         need_mask = (a.causal && a.q_start + r0 < a.kv_start + wk_hi - 1) ||
-                    (r0 + C::BQ > a.len_q) || (wk_lo + 32 > a.len_kv);
+                    (r0 + C::BQ > a.len_q) || (wk_lo + 32 > a.len_kv) ||
+                    a.q_start + r0 + C::BQ - 1 - (a.kv_start + wk_lo) >= a.win;
       if (need_mask) {  // hidden scores -> -inf, so P = exp2(-inf) = 0 (c > 0)
         const int64_t rmin = a.causal ? a.kv_start + key - a.q_start - r0 : INT64_MIN / 2;
-        const int64_t rmax = a.len_q - 1 - r0;
+        const int64_t rmax = min<int64_t>(a.len_q - 1 - r0, a.kv_start + key + a.win - 1 - a.q_start - r0);
         const bool key_ok = key < a.len_kv;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -363,7 +370,12 @@ void dq_bf16_kernel(BwdArgs a) {
     const int64_t lim = a.q_start + (q_hi - 1) - a.kv_start;
     kt_end = lim < 0 ? 0 : int(min<int64_t>(a.n_ktiles, lim / BN + 1));
   }
-  if (kt_end == 0) return;  // uniform: no key visible to any row here
+  int kt_begin = 0;  // first key tile inside the window of the tile's first row
+  {
+    const int64_t lo = a.q_start + q_lo - a.win + 1 - a.kv_start;
+    if (lo > 0) kt_begin = lo >= a.len_kv ? a.n_ktiles : int(lo / BN);
+  }
+  if (kt_begin >= kt_end) return;  // uniform: no key visible to any row here
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -428,11 +440,11 @@ void dq_bf16_kernel(BwdArgs a) {
     }
   };
 
-  stage_tile(0, 0);
+  stage_tile(kt_begin, kt_begin & 1);
   wait_vmem();
   __syncthreads();
 
-  for (int kt = 0; kt < kt_end; ++kt) {
+  for (int kt = kt_begin; kt < kt_end; ++kt) {
     if (kt + 1 < kt_end) stage_tile(kt + 1, (kt + 1) & 1);  // lands while this tile computes
     const lds_u16* Ks = smem + (kt & 1) * C::STAGE;
     const lds_u16* Vs = Ks + C::TILE;
@@ -452,25 +464,29 @@ void dq_bf16_kernel(BwdArgs a) {
         update(Ks, C::NSB - 1, s, dp);
       }
     } else {
-      int nsb = 0;
+      int nsb = 0, kb0 = 0;
       if (wave_active) {
         int64_t vis_last = a.len_kv - 1 - key0;
         if (a.causal) vis_last = min(vis_last, a.q_start + (w_hi - 1) - a.kv_start - key0);
         nsb = vis_last < 0 ? 0 : int(min<int64_t>(C::NSB, vis_last / 32 + 1));
+        const int64_t vis_first = a.q_start + w_lo - a.win + 1 - a.kv_start - key0;
+        if (vis_first > 0) kb0 = int(min<int64_t>(C::NSB, vis_first / 32));
       }
 #pragma unroll 1
-      for (int kb = 0; kb < nsb; ++kb) {
+      for (int kb = kb0; kb < nsb; ++kb) {
         f32x16 s, dp;
         sdp(Ks, Vs, kb, s, dp);
         const int64_t kfirst = key0 + kb * 32;
-        if ((a.causal && a.kv_start + kfirst + 31 > a.q_start + w_lo) || kfirst + 32 > a.len_kv) {
+        if ((a.causal && a.kv_start + kfirst + 31 > a.q_start + w_lo) || kfirst + 32 > a.len_kv ||
+            a.q_start + (w_hi - 1) - (a.kv_start + kfirst) >= a.win) {
           // hidden scores -> -inf, so P = exp2(-inf) = 0 (c > 0)
           int64_t vlim = a.len_kv - 1 - kfirst;
           if (a.causal) vlim = min(vlim, a.q_start + row - a.kv_start - kfirst);
+          const int64_t vmin = a.q_start + row - a.win + 1 - a.kv_start - kfirst;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int off = 8 * (r >> 2) + 4 * hi + (r & 3);
-            if (off > vlim) s[r] = -INFINITY;
+            if (off > vlim || off < vmin) s[r] = -INFINITY;
           }
         }
         update(Ks, kb, s, dp);
@@ -589,6 +605,7 @@ dfa_status launch_bwd(const dfa_attn_desc& d, const void* q, const void* k, cons
   // fp32), and dQ, dK carry the true scale.
   a.c = std::max(d.scale * kLog2e, FLT_MIN);
   a.scale = d.scale;
+  a.win = d.window > 0 ? d.window : kNoWindow;
   if (d.head_dim == 128) return launch_bwd_d<128>(d, a, s, parts);
   return launch_bwd_d<64>(d, a, s, parts);
 }

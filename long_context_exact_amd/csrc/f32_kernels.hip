@@ -33,6 +33,7 @@ struct F32Args {
   int64_t len_q, len_kv, q_start, kv_start;
   int32_t hq, hkv, group, causal;
   float scale;
+  int64_t win;  // sliding window in tokens; a huge value when there is none
 };
 
 // Lanes hold head_dim elements lane and lane + 64 (when D == 128).
@@ -51,11 +52,15 @@ struct Row {
   }
 };
 
-// Number of keys (prefix of the chunk) visible to local query row `row`.
+// Keys [first_key, visible_keys) of the chunk are visible to local query
+// row `row`: the causal prefix, cut below by the sliding window.
 __device__ __forceinline__ int64_t visible_keys(const F32Args& a, int64_t row) {
   if (!a.causal) return a.len_kv;
   const int64_t lim = a.q_start + row - a.kv_start + 1;
   return lim < 0 ? 0 : min(lim, a.len_kv);
+}
+__device__ __forceinline__ int64_t first_key(const F32Args& a, int64_t row) {
+  return max<int64_t>(0, a.q_start + row - a.win + 1 - a.kv_start);
 }
 
 template <int D>
@@ -73,7 +78,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(F32Args a) {
   const float* vb = a.v + b * a.len_kv * kv_rs + int64_t(g) * D;
   float m = -INFINITY, l = 0.f, acc[D / 64] = {};
   const int64_t nk = visible_keys(a, row);
-  for (int64_t j = 0; j < nk; ++j) {
+  for (int64_t j = first_key(a, row); j < nk; ++j) {
     Row<D> k, v;
     k.load(kb + j * kv_rs, lane);
     v.load(vb + j * kv_rs, lane);
@@ -112,7 +117,7 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(F32Args a) {
   const float* vb = a.v + b * a.len_kv * kv_rs + int64_t(g) * D;
   float acc[D / 64] = {};
   const int64_t nk = visible_keys(a, row);
-  for (int64_t j = 0; j < nk; ++j) {
+  for (int64_t j = first_key(a, row); j < nk; ++j) {
     Row<D> k, v;
     k.load(kb + j * kv_rs, lane);
     v.load(vb + j * kv_rs, lane);
@@ -141,10 +146,12 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(F32Args a) {
   v.load(a.v + (b * a.len_kv + j) * kv_rs + int64_t(g) * D, lane);
   int64_t i0 = 0;  // first query row that sees key j
   if (a.causal) i0 = max<int64_t>(0, a.kv_start + j - a.q_start);
+  // rows past the last one whose window reaches key j
+  const int64_t i1 = min<int64_t>(a.len_q, a.kv_start + j + a.win - a.q_start);
   float dk[D / 64] = {}, dv[D / 64] = {};
   for (int hh = 0; hh < a.group; ++hh) {
     const int h = g * a.group + hh;
-    for (int64_t i = i0; i < a.len_q; ++i) {
+    for (int64_t i = i0; i < i1; ++i) {
       const float lse = a.lse[(b * a.hq + h) * a.len_q + i];
       if (!(lse > -INFINITY)) continue;
       Row<D> q, dO;
@@ -178,6 +185,7 @@ F32Args make_args(const dfa_attn_desc& d) {
   a.hkv = d.heads_kv;
   a.group = d.heads_q / d.heads_kv;
   a.causal = d.causal;
+  a.win = d.window > 0 ? d.window : kNoWindow;
   a.scale = d.scale;
   return a;
 }

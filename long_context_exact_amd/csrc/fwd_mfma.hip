@@ -45,6 +45,7 @@ struct FwdArgs {
   int32_t hq, hkv, group, causal;
   int32_t n_qtiles, n_ktiles, n_hgroups;
   float c;  // scale * log2(e), > 0
+  int64_t win;  // sliding window in tokens; a huge value when there is none
 };
 
 template <int D, int NW, int HPW, int BN>
@@ -109,6 +110,12 @@ void fwd_bf16_kernel(FwdArgs a) {
   if (a.causal) {
     const int64_t lim = a.q_start + (q_hi - 1) - a.kv_start;
     kt_end = lim < 0 ? 0 : int(min<int64_t>(a.n_ktiles, lim / BN + 1));
+  }
+  // First key tile inside the window of the tile's first row (App. F).
+  int kt_begin = 0;
+  {
+    const int64_t lo = a.q_start + q_lo - a.win + 1 - a.kv_start;  // lowest visible key
+    if (lo > 0) kt_begin = lo >= a.len_kv ? a.n_ktiles : int(lo / BN);
   }
 
   f32x16 oacc[D / 32];
@@ -195,18 +202,19 @@ void fwd_bf16_kernel(FwdArgs a) {
     }
   };
 
-  if (kt_end > 0) stage_tile(0, 0);
+  if (kt_begin < kt_end) stage_tile(kt_begin, kt_begin & 1);
   wait_vmem();
   __syncthreads();
 
-  for (int kt = 0; kt < kt_end; ++kt) {
+  for (int kt = kt_begin; kt < kt_end; ++kt) {
     if (kt + 1 < kt_end) stage_tile(kt + 1, (kt + 1) & 1);  // lands while this tile computes
     const lds_u16* Ks = smem + (kt & 1) * C::STAGE;
     const lds_u16* Vs = Ks + C::TILE;
     const int64_t key0 = int64_t(kt) * BN;
     if (INSTR && b == 0 && hg == 0 && tid == 0) {
       const int64_t last_k = a.kv_start + min(key0 + BN, a.len_kv) - 1;
-      const bool straddle = a.causal && last_k > a.q_start + q_lo;
+      const bool straddle = a.causal && (last_k > a.q_start + q_lo ||
+                                         a.q_start + q_hi - 1 - (a.kv_start + key0) >= a.win);
       a.visits[int64_t(qt) * a.n_ktiles + kt] = straddle ? 2 : 1;
     }
     if constexpr (FULL) {
@@ -223,25 +231,30 @@ void fwd_bf16_kernel(FwdArgs a) {
         pv(Vs, C::NSB - 1, s_cur);
       }
     } else {
-      // Visible 32-key sub-blocks of this tile for this wave's rows.
-      int nsb = 0;
+      // Visible 32-key sub-blocks of this tile for this wave's rows: up to
+      // the causal limit of the last row, from the window start of the first.
+      int nsb = 0, kb0 = 0;
       if (wave_active) {
         int64_t vis_last = a.len_kv - 1 - key0;  // last key offset inside the chunk
         if (a.causal) vis_last = min(vis_last, a.q_start + (w_hi - 1) - a.kv_start - key0);
         nsb = vis_last < 0 ? 0 : int(min<int64_t>(C::NSB, vis_last / 32 + 1));
+        const int64_t vis_first = a.q_start + w_lo - a.win + 1 - a.kv_start - key0;
+        if (vis_first > 0) kb0 = int(min<int64_t>(C::NSB, vis_first / 32));
       }
 #pragma unroll 1
-      for (int kb = 0; kb < nsb; ++kb) {
+      for (int kb = kb0; kb < nsb; ++kb) {
         f32x16 s = qk(Ks, kb);
         const int64_t kfirst = key0 + kb * 32;
-        if ((a.causal && a.kv_start + kfirst + 31 > a.q_start + w_lo) || kfirst + 32 > a.len_kv) {
+        if ((a.causal && a.kv_start + kfirst + 31 > a.q_start + w_lo) || kfirst + 32 > a.len_kv ||
+            a.q_start + (w_hi - 1) - (a.kv_start + kfirst) >= a.win) {
           // hidden scores become -inf; exp2 of them is exactly 0 (c > 0)
           int64_t vlim = a.len_kv - 1 - kfirst;
           if (a.causal) vlim = min(vlim, a.q_start + row - a.kv_start - kfirst);
+          const int64_t vmin = a.q_start + row - a.win + 1 - a.kv_start - kfirst;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int off = 8 * (r >> 2) + 4 * hi + (r & 3);
-            if (off > vlim) s[r] = -INFINITY;
+            if (off > vlim || off < vmin) s[r] = -INFINITY;
           }
         }
         softmax(s);
@@ -357,6 +370,7 @@ dfa_status launch_fwd(const dfa_attn_desc& d, const void* q, const void* k, cons
   // runs as the smallest normal one, whose scores (|s| * 1.2e-38) still give
   // every visible key the weight exp2(0) = 1 in fp32.
   a.c = std::max(d.scale * kLog2e, FLT_MIN);
+  a.win = d.window > 0 ? d.window : kNoWindow;
   if (d.head_dim == 128) return launch_d<128>(d, a, visits != nullptr, s);
   return launch_d<64>(d, a, visits != nullptr, s);
 }

@@ -37,12 +37,19 @@ dfa_status allow_lds(K kernel, int bytes, const char* what) {
   return DFA_OK;
 }
 
+// Sliding window in the kernels' arguments when the descriptor has none:
+// larger than any token distance (positions are < 2^41), small enough that
+// position arithmetic with it cannot overflow.
+constexpr int64_t kNoWindow = int64_t(1) << 60;
+
 // True when every query row of the pair sees every key (non-causal, or the
 // key chunk ends at or before the first query) and the key chunk is a whole
 // number of `tile` keys: such pairs need no mask anywhere.
 inline bool pair_is_full(const dfa_attn_desc& d, int64_t tile) {
   const bool all_visible = !d.causal || d.kv_start + d.len_kv - 1 <= d.q_start;
-  return all_visible && d.len_kv % tile == 0;
+  // a window must also reach from the last query back to the first key
+  const bool in_window = d.window <= 0 || (d.q_start + d.len_q - 1) - d.kv_start < d.window;
+  return all_visible && in_window && d.len_kv % tile == 0;
 }
 
 // o = 0, lse = -inf for every row (a chunk pair with no keys).

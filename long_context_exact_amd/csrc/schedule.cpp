@@ -59,3 +59,44 @@ extern "C" dfa_status dfa_balanced_schedule(int32_t num_workers, int32_t balance
   }
   return n == total ? DFA_OK : fail(DFA_ERR_INVALID, "dfa_balanced_schedule: internal count");
 }
+
+// Local sliding window (App. F, discussion of sparse attention): a query
+// sees only the `window` tokens ending at itself, so the work per worker is
+// already nearly even; each worker keeps its query chunk and loops only over
+// the key/value chunks that hold keys inside some window of its queries.
+// The pair (w, w - t), t >= 1, has its closest tokens (t - 1) * C + 1 apart
+// and its farthest (t + 1) * C - 1 apart.
+extern "C" dfa_status dfa_window_schedule(int32_t num_workers, int64_t chunk_len, int64_t window,
+                                          dfa_work_item* items, int64_t capacity,
+                                          int64_t* num_items, int32_t* num_steps) {
+  using dfa::fail;
+  const std::string fn = "dfa_window_schedule";
+  if (num_items == nullptr || num_steps == nullptr)
+    return fail(DFA_ERR_INVALID, fn + ": num_items and num_steps must be non-null");
+  if (num_workers < 1 || num_workers > 65536)
+    return fail(DFA_ERR_INVALID, fn + ": num_workers must be in [1, 65536], got " +
+                                     std::to_string(num_workers));
+  if (chunk_len < 1 || window < 1)
+    return fail(DFA_ERR_INVALID, fn + ": chunk_len and window must be >= 1");
+  if (capacity < 0 || (items == nullptr && capacity > 0))
+    return fail(DFA_ERR_INVALID, fn + ": bad capacity / items");
+  const int64_t p = num_workers;
+  // steps: t = 0 plus every t >= 1 with (t - 1) * C + 1 < window, t < P
+  int64_t steps = 1;
+  while (steps < p && (steps - 1) * chunk_len + 1 < window) ++steps;
+  int64_t total = 0;
+  for (int64_t t = 0; t < steps; ++t) total += p - t;
+  *num_items = total;
+  *num_steps = int32_t(steps);
+  if (capacity < total)
+    return fail(DFA_ERR_CAPACITY, fn + ": capacity " + std::to_string(capacity) +
+                                      " < required " + std::to_string(total));
+  int64_t n = 0;
+  for (int64_t t = 0; t < steps; ++t) {
+    // farthest pair (t + 1) * C - 1 apart: inside the window -> full pair
+    const int32_t kind = t == 0 ? 0 : ((t + 1) * chunk_len - 1 < window ? 1 : 2);
+    for (int64_t w = t; w < p; ++w)
+      items[n++] = {int32_t(t), int32_t(w), int32_t(w), int32_t(w - t), kind, int32_t(w)};
+  }
+  return DFA_OK;
+}

@@ -21,13 +21,13 @@ from .build import LIB_PATH
 
 DFA_OK, DFA_ERR_INVALID, DFA_ERR_UNSUPPORTED, DFA_ERR_CAPACITY, DFA_ERR_HIP = range(5)
 DFA_F32, DFA_BF16 = 0, 1
-DIAG, FULL = 0, 1
+DIAG, FULL, BAND = 0, 1, 2
 
 _DTYPES = {"f32": DFA_F32, "bf16": DFA_BF16}
 _TORCH = {DFA_F32: torch.float32, DFA_BF16: torch.bfloat16}
 
 EXPORTED = (
-    "dfa_balanced_schedule", "dfa_attn_fwd_partial", "dfa_lse_merge", "dfa_attn_bwd",
+    "dfa_balanced_schedule", "dfa_window_schedule", "dfa_attn_fwd_partial", "dfa_lse_merge", "dfa_attn_bwd",
     "dfa_last_error", "dfa_version", "dfa_test_tile_shape", "dfa_test_fwd_tile_visits",
     "dfa_test_bwd_part",
 )
@@ -51,17 +51,17 @@ class AttnDesc(ctypes.Structure):
         ("batch", ctypes.c_int32), ("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32),
         ("head_dim", ctypes.c_int32), ("len_q", ctypes.c_int64), ("len_kv", ctypes.c_int64),
         ("q_start", ctypes.c_int64), ("kv_start", ctypes.c_int64), ("causal", ctypes.c_int32),
-        ("scale", ctypes.c_float), ("dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float), ("dtype", ctypes.c_int32), ("window", ctypes.c_int64),
     ]
 
 
 def make_desc(batch, heads_q, heads_kv, head_dim, len_q, len_kv, q_start=0, kv_start=0,
-              causal=True, scale=None, dtype="bf16") -> AttnDesc:
+              causal=True, scale=None, dtype="bf16", window=0) -> AttnDesc:
     if scale is None:
         scale = 1.0 / math.sqrt(head_dim)
     return AttnDesc(int(batch), int(heads_q), int(heads_kv), int(head_dim), int(len_q), int(len_kv),
                     int(q_start), int(kv_start), int(bool(causal)), float(scale),
-                    _DTYPES[dtype] if isinstance(dtype, str) else int(dtype))
+                    _DTYPES[dtype] if isinstance(dtype, str) else int(dtype), int(window))
 
 
 _LIB = None
@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
         P, I32, I64, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
         L.dfa_balanced_schedule.argtypes = [I32, I32, ctypes.POINTER(WorkItem), I64,
                                             ctypes.POINTER(I64), ctypes.POINTER(I32)]
+        L.dfa_window_schedule.argtypes = [I32, I64, I64, ctypes.POINTER(WorkItem), I64,
+                                          ctypes.POINTER(I64), ctypes.POINTER(I32)]
         L.dfa_attn_fwd_partial.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P]
         L.dfa_lse_merge.argtypes = [I32, ctypes.POINTER(P), ctypes.POINTER(P), I32, I32, I64, I32,
                                     I32, P, P, P]
@@ -87,7 +89,7 @@ def lib() -> ctypes.CDLL:
         L.dfa_test_fwd_tile_visits.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P]
         L.dfa_test_bwd_part.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, P, P, I32,
                                         P]
-        for name in ("dfa_balanced_schedule", "dfa_attn_fwd_partial", "dfa_lse_merge",
+        for name in ("dfa_balanced_schedule", "dfa_window_schedule", "dfa_attn_fwd_partial", "dfa_lse_merge",
                      "dfa_attn_bwd", "dfa_test_tile_shape", "dfa_test_fwd_tile_visits",
                      "dfa_test_bwd_part"):
             getattr(L, name).restype = I32
@@ -155,6 +157,21 @@ def dfa_balanced_schedule(num_workers: int, balanced: bool = True):
     arr = (WorkItem * max(n.value, 1))()
     _check(lib().dfa_balanced_schedule(int(num_workers), int(bool(balanced)), arr, n.value,
                                        ctypes.byref(n), ctypes.byref(steps)))
+    return [arr[i].astuple() for i in range(n.value)], int(steps.value)
+
+
+def dfa_window_schedule(num_workers: int, chunk_len: int, window: int):
+    """(items as tuples (step, worker, q_chunk, kv_chunk, kind, owner), num_steps) of the
+    sliding-window schedule."""
+    n = ctypes.c_int64(0)
+    steps = ctypes.c_int32(0)
+    st = lib().dfa_window_schedule(int(num_workers), int(chunk_len), int(window), None, 0,
+                                   ctypes.byref(n), ctypes.byref(steps))
+    if st not in (DFA_OK, DFA_ERR_CAPACITY):
+        _check(st)
+    arr = (WorkItem * max(n.value, 1))()
+    _check(lib().dfa_window_schedule(int(num_workers), int(chunk_len), int(window), arr, n.value,
+                                     ctypes.byref(n), ctypes.byref(steps)))
     return [arr[i].astuple() for i in range(n.value)], int(steps.value)
 
 

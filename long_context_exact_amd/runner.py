@@ -1,7 +1,8 @@
 """Host orchestration of the chunked causal attention on one GPU.
 
 P virtual workers hold P contiguous chunks of C tokens ([DistFlashAttn
-§3.1]).  The schedule (from libdfa's dfa_balanced_schedule) lists the
+§3.1]).  The schedule (from libdfa's dfa_balanced_schedule, or
+dfa_window_schedule for a local sliding window, App. F) lists the
 (query chunk, key/value chunk) pairs; each pair is one dfa_attn_fwd_partial
 call, an owner's partials are combined by dfa_lse_merge in ascending
 key/value chunk order, and the backward replays the owner's pairs through
@@ -35,9 +36,14 @@ class ChunkedCausalAttention:
     dtype: str = "bf16"
     balanced: bool = True
     scale: float | None = None
+    window: int = 0  # 0: full causal attention; > 0: local sliding window of that many tokens
 
     def __post_init__(self):
-        self.items, self.num_steps = dfa.dfa_balanced_schedule(self.workers, self.balanced)
+        if self.window > 0:
+            self.items, self.num_steps = dfa.dfa_window_schedule(self.workers, self.chunk,
+                                                                 self.window)
+        else:
+            self.items, self.num_steps = dfa.dfa_balanced_schedule(self.workers, self.balanced)
         if self.scale is None:
             self.scale = self.head_dim ** -0.5
 
@@ -52,7 +58,7 @@ class ChunkedCausalAttention:
     def desc(self, q_chunk: int, kv_chunk: int) -> dfa.AttnDesc:
         c = self.chunk
         return dfa.make_desc(self.batch, self.heads_q, self.heads_kv, self.head_dim, c, c,
-                             q_chunk * c, kv_chunk * c, True, self.scale, self.dtype)
+                             q_chunk * c, kv_chunk * c, True, self.scale, self.dtype, self.window)
 
     # ---- buffers --------------------------------------------------------
     def q_shape(self):

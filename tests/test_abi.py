@@ -62,6 +62,31 @@ def test_schedule_argument_errors(dfa_lib):
     assert n.value == 10
 
 
+@pytest.mark.parametrize("p", [1, 2, 3, 8, 16, 33])
+@pytest.mark.parametrize("c", [1, 7, 128, 32768])
+@pytest.mark.parametrize("win_of_c", [0.001, 0.5, 1.0, 1.5, 2.0, 5.25])
+def test_window_schedule_bit_exact_vs_oracle(dfa_lib, p, c, win_of_c):
+    win = max(1, int(win_of_c * c))
+    for w_ in {win, win + 1, max(1, win - 1)}:
+        items, steps = dfa_lib.dfa_window_schedule(p, c, w_)
+        ref, ref_steps = oracle.window_schedule(p, c, w_)
+        assert steps == ref_steps
+        assert items == [tuple(x) for x in ref]
+
+
+def test_window_schedule_argument_errors(dfa_lib):
+    L = dfa_lib.lib()
+    n, s = ctypes.c_int64(-1), ctypes.c_int32(-1)
+    for args in ((0, 4, 4), (4, 0, 4), (4, 4, 0), (70000, 4, 4)):
+        assert L.dfa_window_schedule(*args, None, 0, ctypes.byref(n), ctypes.byref(s)) == \
+            D.DFA_ERR_INVALID
+        assert dfa_lib.dfa_last_error().startswith("dfa_window_schedule")
+    arr = (D.WorkItem * 3)()
+    assert L.dfa_window_schedule(8, 4, 4, arr, 3, ctypes.byref(n), ctypes.byref(s)) == \
+        D.DFA_ERR_CAPACITY
+    assert n.value == 15 and s.value == 2
+
+
 def _fwd(L, d, q=FAKE, o=FAKE, lse=FAKE):
     return L.dfa_attn_fwd_partial(ctypes.byref(d) if d is not None else None, q, FAKE, FAKE, o,
                                   lse, None)
@@ -79,6 +104,7 @@ def _fwd(L, d, q=FAKE, o=FAKE, lse=FAKE):
     ("scale", float("inf"), D.DFA_ERR_INVALID),
     ("dtype", 7, D.DFA_ERR_INVALID),
     ("batch", -1, D.DFA_ERR_INVALID),
+    ("window", -1, D.DFA_ERR_INVALID),
 ])
 def test_fwd_descriptor_errors(dfa_lib, field, value, status):
     L = dfa_lib.lib()
@@ -86,6 +112,13 @@ def test_fwd_descriptor_errors(dfa_lib, field, value, status):
     setattr(d, field, value)
     assert _fwd(L, d) == status
     assert dfa_lib.dfa_last_error().startswith("dfa_attn_fwd_partial")
+
+
+def test_window_needs_causal(dfa_lib):
+    L = dfa_lib.lib()
+    d = D.make_desc(1, 4, 2, 128, 256, 256, causal=False, window=64)
+    assert _fwd(L, d) == D.DFA_ERR_INVALID
+    assert "window" in dfa_lib.dfa_last_error()
 
 
 def test_fwd_pointer_errors(dfa_lib):
