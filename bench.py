@@ -69,6 +69,19 @@ def pairs_of(kind: int, c: int) -> int:
     return c * (c + 1) // 2 if kind == 0 else c * c
 
 
+def visible_pairs(item, c: int, window: int) -> int:
+    """(query, key) pairs of a chunk pair that the mask keeps: the causal
+    prefix, cut to the keys less than `window` positions behind the query."""
+    if window <= 0:
+        return pairs_of(item[4], c)
+    import numpy as np
+    qpos = item[2] * c + np.arange(c, dtype=np.int64)
+    k0 = item[3] * c
+    hi = np.minimum(c - 1, qpos - k0)                # last visible key (local)
+    lo = np.maximum(0, qpos - window + 1 - k0)       # first visible key (local)
+    return int(np.maximum(hi - lo + 1, 0).sum())
+
+
 def gen_inputs(w, chunks_q, chunks_kv, backward):
     """Seeded per-chunk inputs (numpy float32, bf16-exact), drawn in threads."""
     import concurrent.futures as cf
@@ -96,8 +109,10 @@ def cpu_baseline(w, host, worker, budget_s):
 
     a = worker if worker >= 0 else w.workers - 1
     c = w.chunk
-    kpre = np.concatenate([host[1][j][:, :, :1] for j in range(a + 1)], axis=1).astype(np.float64)
-    vpre = np.concatenate([host[2][j][:, :, :1] for j in range(a + 1)], axis=1).astype(np.float64)
+    kvc = sorted(j for j in host[1] if j <= a)   # the key chunks the rows' keys live in
+    k0 = kvc[0] * c
+    kpre = np.concatenate([host[1][j][:, :, :1] for j in kvc], axis=1).astype(np.float64)
+    vpre = np.concatenate([host[2][j][:, :, :1] for j in kvc], axis=1).astype(np.float64)
 
     def run(r):
         q = host[0][a][:, c - r:, :1].astype(np.float64)
@@ -105,11 +120,13 @@ def cpu_baseline(w, host, worker, budget_s):
             np.ones_like(q)
         q0 = a * c + c - r
         t0 = time.perf_counter()
-        o, lse = oracle.attention_fwd(q, kpre, vpre, w.scale, True, q0, 0)
+        o, lse = oracle.attention_fwd(q, kpre, vpre, w.scale, True, q0, k0, window=w.window)
         t1 = time.perf_counter()
-        oracle.attention_bwd(q, kpre, vpre, o, lse, do, w.scale, True, q0, 0)
+        oracle.attention_bwd(q, kpre, vpre, o, lse, do, w.scale, True, q0, k0, window=w.window)
         t2 = time.perf_counter()
-        pairs = sum(q0 + i + 1 for i in range(r))
+        pos = q0 + np.arange(r)
+        seen = pos - k0 + 1 if w.window <= 0 else np.minimum(w.window, pos - k0 + 1)
+        pairs = int(seen.sum())
         return t2 - t0, pairs * 14 * w.head_dim, (t1 - t0, pairs * 4 * w.head_dim), \
             (t2 - t1, pairs * 10 * w.head_dim)
 
@@ -128,7 +145,8 @@ def cpu_baseline(w, host, worker, budget_s):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads or 1),
             "kind": "oracle",
             "sample": f"float64 numpy oracle ({lib}), fwd+bwd of the last {r} query rows of chunk "
-                      f"{a}, query head 0, over their full causal prefix ({a * c + c} keys); "
+                      f"{a}, query head 0, over every key they see (keys {k0}..{a * c + c - 1}"
+                      f"{f', window {w.window}' if w.window else ''}); "
                       f"{dt:.1f} s, {flops:.3e} algorithmic FLOP",
             "fwd_gflops": round(fw[1] / fw[0] / 1e9, 2), "bwd_gflops": round(bw[1] / bw[0] / 1e9, 2)}
 
@@ -175,7 +193,7 @@ def main():
     dev = "cuda"
     td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     att = ChunkedCausalAttention(w.workers, w.chunk, w.batch, w.heads_q, w.heads_kv, w.head_dim,
-                                 w.dtype, True)
+                                 w.dtype, True, window=w.window)
     if w.share_of >= 0:
         owners = [w.share_of]
         timed = att.items_of_worker(w.share_of)
@@ -220,8 +238,9 @@ def main():
             att.backward_items(timed, q, k, v, o, lse, d_o, delta, dq, dk, dv)
 
     per_pair = w.batch * w.heads_q * w.head_dim
-    fwd_flop = sum(pairs_of(it[4], w.chunk) for it in timed) * per_pair * 4
-    bwd_flop = sum(pairs_of(it[4], w.chunk) for it in timed) * per_pair * 10 if w.backward else 0
+    n_pairs = sum(visible_pairs(it, w.chunk, w.window) for it in timed)
+    fwd_flop = n_pairs * per_pair * 4
+    bwd_flop = n_pairs * per_pair * 10 if w.backward else 0
     flop = fwd_flop + bwd_flop
 
     for _ in range(args.warmup):
@@ -266,7 +285,7 @@ def main():
                                                 v[it[3]], lse[it[2]], d_o[it[2]], delta[it[2]],
                                                 dq[it[2]], dk[it[3]], dv[it[3]], part)
 
-    pairs_x_heads = sum(pairs_of(it[4], w.chunk) for it in timed) * w.batch * w.heads_q
+    pairs_x_heads = n_pairs * w.batch * w.heads_q
     # name in the profiler, time per step, flop per step (the kernel's own
     # contractions on unmasked pairs: forward 2 = 4d, dK/dV 4 = 8d, dQ 3 = 6d)
     names = KERNEL_NAMES if w.dtype == "bf16" else KERNEL_NAMES_F32
@@ -300,7 +319,7 @@ def main():
                    "head_dim": w.head_dim, "batch": w.batch,
                    "share": (f"worker {w.share_of} of {w.workers}" if w.share_of >= 0
                              else "all pairs"),
-                   "pairs_timed": len(timed), "backward": w.backward,
+                   "pairs_timed": len(timed), "backward": w.backward, "window": w.window,
                    "algorithmic_flop_per_step": flop, "wall_s_timed": round(wall, 3),
                    "input_gen_s": round(gen_s, 1)},
         "roofline": roofline,

@@ -66,6 +66,7 @@ class Workload:
     backward: bool      # fwd + bwd (True) or fwd only
     share_of: int       # -1: every chunk pair; w: worker w's share only
     batch: int = 1
+    window: int = 0     # 0: full causal attention; > 0: local sliding window (tokens)
 
     @property
     def total_len(self) -> int:
@@ -86,13 +87,16 @@ class Workload:
         return chunk_tensor(self.seed, tensor_id, chunk, shape, self.dtype)
 
 
-# The five workloads: a tiny fp32 case, three Llama-7B-shaped (32 x 128)
-# bf16 cases and a grouped-query (64 query heads over 8 key/value heads)
-# worker share at a 32768-token chunk.
+# The workloads: a tiny fp32 case, three Llama-7B-shaped (32 x 128) bf16
+# cases, a grouped-query (64 query heads over 8 key/value heads) worker share
+# at a 32768-token chunk, and that share under a local sliding window.
 WORKLOADS = {
     "tiny_f32": Workload("tiny_f32", 128, 4, 2, 2, 64, "f32", 1001, True, -1),
     "llama7b_32k_fwd": Workload("llama7b_32k_fwd", 4096, 8, 32, 32, 128, "bf16", 1002, False, -1),
     "llama7b_64k": Workload("llama7b_64k", 8192, 8, 32, 32, 128, "bf16", 1003, True, -1),
     "llama7b_256k_w15": Workload("llama7b_256k_w15", 16384, 16, 32, 32, 128, "bf16", 1004, True, 15),
     "gqa64x8_512k_w15": Workload("gqa64x8_512k_w15", 32768, 16, 64, 8, 128, "bf16", 1005, True, 15),
+    # the same worker share under a local sliding window of 4096 tokens
+    "gqa64x8_512k_win4k_w15": Workload("gqa64x8_512k_win4k_w15", 32768, 16, 64, 8, 128, "bf16",
+                                       1006, True, 15, window=4096),
 }

@@ -183,3 +183,44 @@ def test_worker_share_forward_backward(name):
     c = w.chunk
     _check_rows(w, host, res, a, [0, 1, c // 2, c - 1], [0, w.heads_q - 1], True)
     _check_grad_identities(w, host, res, [a], kvs)
+
+
+def test_windowed_worker_share_forward_backward():
+    """Worker 15's share under a 4096-token sliding window (App. F): the
+    window schedule gives it (15, 15) and (15, 14) only; sampled rows of the
+    merged O / LSE and of dQ against the oracle over each row's window, and
+    the dK / dV identities over the two key chunks."""
+    w = WORKLOADS["gqa64x8_512k_win4k_w15"]
+    print(f"case {w.name}", flush=True)
+    att = ChunkedCausalAttention(w.workers, w.chunk, w.batch, w.heads_q, w.heads_kv, w.head_dim,
+                                 w.dtype, window=w.window)
+    a, c, win = w.share_of, w.chunk, w.window
+    items = att.items_of_owner(a)
+    assert [it[3] for it in items] == [a - 1, a] and sorted(att.items_of_worker(a)) == sorted(items)
+    kvs = [a - 1, a]
+    host = _inputs(w, [a], kvs)
+    res = _run(w, att, host, [a], items, True)
+    grp = w.heads_q // w.heads_kv
+    got_o, want_o, got_dq, want_dq = [], [], [], []
+    for h in (0, w.heads_q - 1):
+        g = h // grp
+        kp = np.concatenate([host[1][j][:, :, g:g + 1] for j in kvs], 1).astype(np.float64)
+        vp = np.concatenate([host[2][j][:, :, g:g + 1] for j in kvs], 1).astype(np.float64)
+        for r in (0, 1, win - 2, win - 1, win, c // 2, c - 1):
+            qr = host[0][a][:, r:r + 1, h:h + 1].astype(np.float64)
+            ro, rl = oracle.attention_fwd(qr, kp, vp, w.scale, True, a * c + r, (a - 1) * c,
+                                          window=win)
+            got_o.append(to_np(res["o"][a][:, r, h]).ravel())
+            want_o.append(ro.ravel())
+            check_lse(to_np(res["lse"][a][:, h, r]).reshape(rl.shape), rl, "bf16",
+                      f"LSE row {r} head {h}")
+            dor = host[3][a][:, r:r + 1, h:h + 1].astype(np.float64)
+            rq = oracle.attention_bwd(qr, kp, vp, ro, rl, dor, w.scale, True, a * c + r,
+                                      (a - 1) * c, window=win)[0]
+            got_dq.append(to_np(res["dq"][a][:, r, h]).ravel())
+            want_dq.append(rq.ravel())
+    go, wo = np.concatenate(got_o), np.concatenate(want_o)
+    assert np.max(np.abs(go - wo)) <= 1e-2
+    assert rel_fro(go, wo) <= 2e-2
+    assert rel_fro(np.concatenate(got_dq), np.concatenate(want_dq)) <= 2e-2
+    _check_grad_identities(w, host, res, [a], kvs)
