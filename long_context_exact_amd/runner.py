@@ -104,3 +104,84 @@ class ChunkedCausalAttention:
                              d_o[a], delta[a], first, dq[a], dk[c], dv[c], stream)
             have.add(a)
         return have
+
+    # ---- communication / computation overlap (one GPU, two streams) -------
+    def forward_worker_overlapped(self, w, q, k, v, partials, overlap=True):
+        """Worker w's forward items in step order with the per-step exchange
+        emulated on a second stream ([DistFlashAttn §3.2]: the next block's
+        key/value tensors are prefetched while the current block computes, on
+        separate streams; §1, Fig. 2).
+
+        An owner item (w, c), c != w, needs chunk c's K and V from worker c;
+        a helper item (a, w) needs owner a's Q and sends its (O, LSE) back.
+        Each received tensor lands in one of two receive slots by a
+        device-to-device copy on the communication stream; the copy for step
+        t + 1 is issued before step t computes, and a slot is refilled only
+        after the compute that read it finished (events).  A helper's result
+        goes back to the owner's buffer on the communication stream.  With
+        overlap=False every copy runs on the compute stream, in line with
+        the computation (the non-overlapped baseline).  Results are bitwise
+        those of `forward_items`."""
+        items = sorted(self.items_of_worker(w), key=lambda it: it[0])
+        dev = q[w].device
+        compute = torch.cuda.current_stream(dev)
+        comm = torch.cuda.Stream(dev) if overlap else compute
+        # receive slots and the helper's local output, allocated on the
+        # compute stream and marked as used by the communication stream
+        slots = [{"q": torch.empty_like(q[w]), "k": torch.empty_like(k[w]),
+                  "v": torch.empty_like(v[w])} for _ in range(2)]
+        helper_out = [self.new_partial(dev) for _ in range(2)]  # double-buffered returns
+        back = [None, None]          # return-copy events of each helper buffer
+        if overlap:
+            for t in [x for sl in slots for x in sl.values()] + [y for h in helper_out for y in h]:
+                t.record_stream(comm)
+        done = [None, None]          # compute events that last read each slot
+        ready = {}                   # step index -> copy-complete event
+
+        def post_copy(i):
+            a, c = items[i][2], items[i][3]
+            sl = slots[i % 2]
+            with torch.cuda.stream(comm):
+                if done[i % 2] is not None:
+                    comm.wait_event(done[i % 2])
+                if a != w:      # helper: the owner's queries come in
+                    sl["q"].copy_(q[a], non_blocking=True)
+                elif c != w:    # owner: the key/value chunk comes in
+                    sl["k"].copy_(k[c], non_blocking=True)
+                    sl["v"].copy_(v[c], non_blocking=True)
+                ev = torch.cuda.Event()
+                ev.record(comm)
+                ready[i] = ev
+
+        nh = 0                       # helper items so far
+        if items:
+            post_copy(0)
+        for i, it in enumerate(items):
+            if i + 1 < len(items):
+                post_copy(i + 1)
+            a, c = it[2], it[3]
+            sl = slots[i % 2]
+            compute.wait_event(ready[i])
+            qa = sl["q"] if a != w else q[a]
+            kc, vc = (sl["k"], sl["v"]) if (a == w and c != w) else (k[c], v[c])
+            if a != w:
+                hb = nh % 2
+                if back[hb] is not None:
+                    compute.wait_event(back[hb])  # its previous result has been sent
+                out = helper_out[hb]
+            else:
+                out = partials[(a, c)]
+            dfa.dfa_attn_fwd_partial(self.desc(a, c), qa, kc, vc, *out)
+            ev = torch.cuda.Event()
+            ev.record(compute)
+            done[i % 2] = ev
+            if a != w:  # send the helper's (O, LSE) back to the owner
+                with torch.cuda.stream(comm):
+                    comm.wait_event(ev)
+                    for dst, src in zip(partials[(a, c)], out):
+                        dst.copy_(src, non_blocking=True)
+                    back[hb] = torch.cuda.Event()
+                    back[hb].record(comm)
+                nh += 1
+        if overlap:
+            compute.wait_stream(comm)

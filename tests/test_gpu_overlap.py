@@ -1,0 +1,40 @@
+"""The two-stream exchange emulation ([DistFlashAttn §3.2]: key/value
+prefetch on a separate stream, overlapped with compute) gives bitwise the
+results of the plain forward, for owners and for helpers whose results are
+sent back to their owners."""
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_exact_amd.runner import ChunkedCausalAttention
+
+from _util import rand, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu(dfa_lib):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.mark.parametrize("p,c,window", [(5, 160, 0), (4, 128, 0), (4, 128, 200)])
+def test_overlapped_worker_forward_is_bitwise_plain(p, c, window):
+    print(f"case overlap {p} {c} {window}", flush=True)
+    rng = np.random.default_rng(p * 10 + c)
+    att = ChunkedCausalAttention(p, c, 1, 4, 2, 128, "bf16", window=window)
+    q = {a: to_dev(rand(rng, att.q_shape(), "bf16"), "bf16") for a in range(p)}
+    k = {a: to_dev(rand(rng, att.kv_shape(), "bf16"), "bf16") for a in range(p)}
+    v = {a: to_dev(rand(rng, att.kv_shape(), "bf16"), "bf16") for a in range(p)}
+    ref = {(it[2], it[3]): att.new_partial() for it in att.items}
+    att.forward_items(att.items, q, k, v, ref)
+    for overlap in (True, False):
+        got = {key: (torch.full_like(o, 7.0), torch.full_like(l_, 7.0)) for key, (o, l_) in ref.items()}
+        for w in range(p):
+            att.forward_worker_overlapped(w, q, k, v, got, overlap=overlap)
+        torch.cuda.synchronize()
+        for key in ref:
+            assert torch.equal(got[key][0], ref[key][0]), (overlap, key)
+            assert torch.equal(got[key][1], ref[key][1]), (overlap, key)
