@@ -197,8 +197,10 @@ void dkdv_bf16_kernel(BwdArgs a) {
           y[e] = ok ? a.delta[lbase + 8 * r4 + 4 * hi + e] : 0.f;
         }
       }
+      // every row of a fully visible pair sees keys, so its LSE is finite
 #pragma unroll
-      for (int e = 0; e < 4; ++e) nl[r4][e] = x[e] > -INFINITY ? -x[e] * kLog2e : -INFINITY;
+      for (int e = 0; e < 4; ++e)
+        nl[r4][e] = (FULL || x[e] > -INFINITY) ? -x[e] * kLog2e : -INFINITY;
       dl[r4] = y;
     }
   };
