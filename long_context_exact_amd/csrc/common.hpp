@@ -42,6 +42,12 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 
 // Value of `x` held by lane (l ^ 32) of the wave.
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+// max(x, x of lane l ^ 32) in one v_permlane32_swap (no LDS round trip).
+__device__ __forceinline__ float max_xor32(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, unsigned(r[0])), __builtin_bit_cast(float, unsigned(r[1])));
+}
 
 __device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));

@@ -161,13 +161,15 @@ void fwd_bf16_kernel(FwdArgs a) {
     return s;
   };
   // Online-softmax update with the sub-block's scores (hidden ones -inf);
-  // leaves P in s.
+  // leaves P in s.  The reference point m (log2 units) moves only when the
+  // row max exceeds it by more than 8, so P <= 2^8 and rescaling the
+  // accumulators is rare; O and the LSE do not depend on m.
   auto softmax = [&](f32x16& s) {
     float mx = s[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-    mx = fmaxf(mx, xor32(mx));
-    const float m_new = (mx == -INFINITY) ? m : fmaxf(m, mx * a.c);
+    mx = max_xor32(mx);
+    const float m_new = (mx * a.c > m + 8.f) ? mx * a.c : m;
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     float lsum = 0.f;
 #pragma unroll
@@ -220,7 +222,7 @@ void fwd_bf16_kernel(FwdArgs a) {
     if constexpr (FULL) {
       if (wave_active) {
         f32x16 s_cur = qk(Ks, 0);
-#pragma unroll 1
+#pragma unroll  // unrolled: s_cur / s_nxt rename instead of being copied
         for (int kb = 0; kb < C::NSB - 1; ++kb) {
           f32x16 s_nxt = qk(Ks, kb + 1);  // independent of the softmax below
           softmax(s_cur);
