@@ -58,12 +58,11 @@ __device__ __forceinline__ float lse2_of(float lse) {
 #endif
 
 // ---------------------------------------------------------------- dK, dV
-// The workgroup's K and V rows stay in LDS for the whole run (MFMA B operands
-// read per block), Q and dO come in double-buffered 32-row stages, and each
-// lane reads the LSE / delta of its 16 rows straight from memory (tiny and
-// L2-resident; the block's 16 S / dP instructions cover the latency).  This
-// fills exactly 160 KiB of LDS and leaves the register budget of two waves
-// per SIMD to the dK^T / dV^T accumulators.
+// Each wave keeps its 32 keys' K rows in VGPRs (the B operand of S for the
+// whole run); the workgroup's V rows stay in LDS, Q and dO come in
+// double-buffered 32-row stages, and wave 0 stages each step's row
+// statistics (-log2 e * LSE and delta) into the same stage, so no wave
+// holds them in registers between steps.
 template <int D, int NW>
 struct DkvCfg {
   static constexpr int NT = NW * 64;
@@ -73,8 +72,9 @@ struct DkvCfg {
   static constexpr int KV_SEGS = KV_TILE / 512; // 1 KiB segments
   static constexpr int Q_TILE = BQ * D;         // elements of one Q (or dO) tile
   static constexpr int Q_SEGS = Q_TILE / 512;
-  static constexpr int STAGE = 2 * Q_TILE;      // Q + dO (elements)
-  static constexpr int LDS_BYTES = (2 * KV_TILE + 2 * STAGE) * 2;
+  static constexpr int STATS = 2 * BQ;           // -log2 LSE and delta of a step's rows (floats)
+  static constexpr int STAGE = 2 * Q_TILE + 2 * STATS;  // Q + dO + row statistics (16-bit units)
+  static constexpr int LDS_BYTES = (KV_TILE + 2 * STAGE) * 2;
   static_assert(KV_SEGS % NW == 0, "key tile segments must divide over the waves");
   static_assert(Q_SEGS % NW == 0 || NW % Q_SEGS == 0, "query segments over the waves");
   static_assert(LDS_BYTES <= 160 * 1024, "fits gfx950 LDS");
@@ -86,8 +86,7 @@ void dkdv_bf16_kernel(BwdArgs a) {
   using C = DkvCfg<D, NW>;
   extern __shared__ __align__(16) uint16_t smem_generic[];
   lds_u16* smem = lds_base(smem_generic);
-  lds_u16* Ks = smem;
-  lds_u16* Vs = Ks + C::KV_TILE;
+  lds_u16* Vs = smem;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
@@ -118,16 +117,19 @@ void dkdv_bf16_kernel(BwdArgs a) {
   const int nq = int(cdiv(i_end, C::BQ)) - qt0;
   const int steps = a.group * nq;
 
-  {  // the workgroup's K and V rows, once
-    const uint16_t* kb = a.k + b * a.len_kv * kv_rs + int64_t(g) * D;
+  // K of this lane's key as the B operand of S (elements d = 16*st + 8*hi
+  // + e), in VGPRs for the whole loop; V rows of the workgroup in LDS.
+  bf16x8 kf[D / 16];
+  {
+    const uint16_t* kp = a.k + (b * a.len_kv + key) * kv_rs + int64_t(g) * D;
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st)
+      kf[st] = key < a.len_kv ? ld_bf16x8(kp + 16 * st + 8 * hi) : bf16x8{};
     const uint16_t* vb = a.v + b * a.len_kv * kv_rs + int64_t(g) * D;
     const int64_t last = a.len_kv - 1;  // rows past the chunk re-read its last key (masked)
 #pragma unroll
     for (int i = 0; i < C::KV_SEGS / NW; ++i) {
       const int seg = wave * (C::KV_SEGS / NW) + i;
-      tile_dma_segment<D>(Ks, seg, lane, [&](int r) {
-        return kb + min<int64_t>(k_lo + r, last) * kv_rs;
-      });
       tile_dma_segment<D>(Vs, seg, lane, [&](int r) {
         return vb + min<int64_t>(k_lo + r, last) * kv_rs;
       });
@@ -141,7 +143,7 @@ void dkdv_bf16_kernel(BwdArgs a) {
     dv_acc[db] = f32x16{};
   }
 
-  auto stage_ptr = [&](int stage) { return smem + 2 * C::KV_TILE + stage * C::STAGE; };
+  auto stage_ptr = [&](int stage) { return smem + C::KV_TILE + stage * C::STAGE; };
   auto stage_q = [&](int it, int stage) {
     const int h = g * a.group + it / nq;
     const int64_t i0 = int64_t(qt0 + it % nq) * C::BQ;
@@ -174,47 +176,44 @@ void dkdv_bf16_kernel(BwdArgs a) {
     }
   };
 
-  // LSE and delta of this lane's 16 rows of step `it` (rows 8*(r/4) + 4*hi +
-  // r%4 of the step): LSE in -log2 form (P = exp2(fma(s, c, nl))), rows
-  // without keys or past the chunk give nl = -inf, so P = 0.
-  f32x4 nl[4], dl[4];
-  auto load_rows = [&](int it) {
+  // Row statistics of a step, staged by wave 0 into the step's LDS stage:
+  // lane r < 32 holds -log2(e) * LSE of row r (-inf for rows without keys or
+  // past the chunk, so that P = exp2(fma(s, c, nl)) = 0), lane 32 + r holds
+  // delta of row r.  Every wave then reads its lanes' rows from LDS.
+  float stat_v = 0.f;
+  auto load_stats = [&](int it) {
     const int h = g * a.group + it / nq;
-    const int64_t r0 = int64_t(qt0 + it % nq) * C::BQ;
-    const int64_t lbase = (b * a.hq + h) * a.len_q + r0;
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int64_t rr = r0 + 8 * r4 + 4 * hi;
-      f32x4 x, y;
-      if (FULL || rr + 3 < a.len_q) {
-        x = *reinterpret_cast<const f32x4*>(a.lse + lbase + 8 * r4 + 4 * hi);
-        y = *reinterpret_cast<const f32x4*>(a.delta + lbase + 8 * r4 + 4 * hi);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool ok = rr + e < a.len_q;
-          x[e] = ok ? a.lse[lbase + 8 * r4 + 4 * hi + e] : -INFINITY;
-          y[e] = ok ? a.delta[lbase + 8 * r4 + 4 * hi + e] : 0.f;
-        }
-      }
+    const int64_t row = int64_t(qt0 + it % nq) * C::BQ + l32;
+    const int64_t li = (b * a.hq + h) * a.len_q + row;
+    const bool ok = FULL || row < a.len_q;
+    if (hi == 0) {
+      const float x = ok ? a.lse[li] : -INFINITY;
       // every row of a fully visible pair sees keys, so its LSE is finite
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        nl[r4][e] = (FULL || x[e] > -INFINITY) ? -x[e] * kLog2e : -INFINITY;
-      dl[r4] = y;
+      stat_v = (FULL || x > -INFINITY) ? -x * kLog2e : -INFINITY;
+    } else {
+      stat_v = ok ? a.delta[li] : 0.f;
     }
+  };
+  auto store_stats = [&](int stage) {
+    lds_f32* st = reinterpret_cast<lds_f32*>(stage_ptr(stage) + 2 * C::Q_TILE);
+    st[lane] = stat_v;
   };
 
   stage_q(0, 0);
+  if (wave == 0) load_stats(0);
   wait_vmem();
-  load_rows(0);
+  if (wave == 0) store_stats(0);
   __syncthreads();
 
 #pragma unroll 1
   for (int it = 0; it < steps; ++it) {
-    if (it + 1 < steps) stage_q(it + 1, (it + 1) & 1);  // lands while this step computes
+    if (it + 1 < steps) {  // lands while this step computes
+      stage_q(it + 1, (it + 1) & 1);
+      if (wave == 0) load_stats(it + 1);
+    }
     const lds_u16* Qs = stage_ptr(it & 1);
     const lds_u16* dOs = Qs + C::Q_TILE;
+    const lds_f32* stats = reinterpret_cast<const lds_f32*>(Qs + 2 * C::Q_TILE);
     const int64_t r0 = int64_t(qt0 + it % nq) * C::BQ;  // first row of this step
     bool any = wave_active;
     if constexpr (!FULL) {
@@ -227,7 +226,7 @@ void dkdv_bf16_kernel(BwdArgs a) {
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int st = 0; st < D / 16; ++st)
-        s = mfma32(tile_row8<D>(Qs, l32, 2 * st + hi), tile_row8<D>(Ks, wave * 32 + l32, 2 * st + hi), s);
+        s = mfma32(tile_row8<D>(Qs, l32, 2 * st + hi), kf[st], s);
 #pragma unroll
       for (int st = 0; st < D / 16; ++st)
         dp = mfma32(tile_row8<D>(dOs, l32, 2 * st + hi), tile_row8<D>(Vs, wave * 32 + l32, 2 * st + hi), dp);
@@ -247,8 +246,13 @@ void dkdv_bf16_kernel(BwdArgs a) {
         }
       }
       // P, then dV^T += dO^T P; dS is formed while those instructions run.
+      // This lane's rows are 8 * (r / 4) + 4 * hi + r % 4.
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = exp2_fast(fmaf(s[r], a.c, nl[r >> 2][r & 3]));
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 nl = *reinterpret_cast<const DFA_LDS f32x4*>(stats + 8 * r4 + 4 * hi);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[4 * r4 + e] = exp2_fast(fmaf(s[4 * r4 + e], a.c, nl[e]));
+      }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         bf16x8 pb;
@@ -263,7 +267,11 @@ void dkdv_bf16_kernel(BwdArgs a) {
         }
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dp[r] = s[r] * (dp[r] - dl[r >> 2][r & 3]);
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 dl = *reinterpret_cast<const DFA_LDS f32x4*>(stats + C::BQ + 8 * r4 + 4 * hi);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dp[4 * r4 + e] = s[4 * r4 + e] * (dp[4 * r4 + e] - dl[e]);
+      }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         bf16x8 sb;
@@ -278,12 +286,11 @@ void dkdv_bf16_kernel(BwdArgs a) {
         }
       }
     }
-    // The next stage this wave staged must land before the barrier; the next
-    // step's LSE / delta rows are issued after that wait, so their latency
-    // hides behind the barrier and the next S / dP.
+    // The next stage this wave staged (and, for wave 0, the next step's row
+    // statistics) must land before the barrier.
     if (it + 1 < steps) {
       wait_vmem();
-      load_rows(it + 1);
+      if (wave == 0) store_stats((it + 1) & 1);
     }
     __syncthreads();
   }
