@@ -180,23 +180,24 @@ void dkdv_bf16_kernel(BwdArgs a) {
   // lane r < 32 holds -log2(e) * LSE of row r (-inf for rows without keys or
   // past the chunk, so that P = exp2(fma(s, c, nl)) = 0), lane 32 + r holds
   // delta of row r.  Every wave then reads its lanes' rows from LDS.
-  float stat_v = 0.f;
+  static_assert(C::BQ <= 64, "one lane per row of a step");
+  float stat_l = 0.f, stat_d = 0.f;
   auto load_stats = [&](int it) {
     const int h = g * a.group + it / nq;
-    const int64_t row = int64_t(qt0 + it % nq) * C::BQ + l32;
+    const int64_t row = int64_t(qt0 + it % nq) * C::BQ + lane;
     const int64_t li = (b * a.hq + h) * a.len_q + row;
-    const bool ok = FULL || row < a.len_q;
-    if (hi == 0) {
-      const float x = ok ? a.lse[li] : -INFINITY;
-      // every row of a fully visible pair sees keys, so its LSE is finite
-      stat_v = (FULL || x > -INFINITY) ? -x * kLog2e : -INFINITY;
-    } else {
-      stat_v = ok ? a.delta[li] : 0.f;
-    }
+    const bool ok = lane < C::BQ && (FULL || row < a.len_q);
+    const float x = ok ? a.lse[li] : -INFINITY;
+    // every row of a fully visible pair sees keys, so its LSE is finite
+    stat_l = (FULL || x > -INFINITY) ? -x * kLog2e : -INFINITY;
+    stat_d = ok ? a.delta[li] : 0.f;
   };
   auto store_stats = [&](int stage) {
     lds_f32* st = reinterpret_cast<lds_f32*>(stage_ptr(stage) + 2 * C::Q_TILE);
-    st[lane] = stat_v;
+    if (lane < C::BQ) {
+      st[lane] = stat_l;
+      st[C::BQ + lane] = stat_d;
+    }
   };
 
   stage_q(0, 0);
@@ -217,7 +218,7 @@ void dkdv_bf16_kernel(BwdArgs a) {
     const int64_t r0 = int64_t(qt0 + it % nq) * C::BQ;  // first row of this step
     bool any = wave_active;
     if constexpr (!FULL) {
-      if (any && a.causal) any = a.q_start + min(r0 + C::BQ, a.len_q) - 1 >= a.kv_start + wk_lo;
+      if (any && a.causal) any = a.q_start + min<int64_t>(r0 + C::BQ, a.len_q) - 1 >= a.kv_start + wk_lo;
       if (any) any = a.q_start + r0 - (a.kv_start + wk_hi - 1) < a.win;
     }
     if (any) {
