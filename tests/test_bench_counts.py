@@ -1,0 +1,37 @@
+"""The FLOP convention of bench.py: visible (query, key) pairs of a chunk pair,
+counted in closed form, against brute-force enumeration on small chunks."""
+
+import importlib.util
+import os
+
+import pytest
+
+import oracle
+
+_spec = importlib.util.spec_from_file_location(
+    "bench", os.path.join(os.path.dirname(os.path.dirname(__file__)), "bench.py"))
+bench = importlib.util.module_from_spec(_spec)
+_spec.loader.exec_module(bench)
+
+
+def _brute(a, c_, chunk, window):
+    n = 0
+    for i in range(chunk):
+        for j in range(chunk):
+            d = (a * chunk + i) - (c_ * chunk + j)
+            if d >= 0 and (window <= 0 or d < window):
+                n += 1
+    return n
+
+
+@pytest.mark.parametrize("p,chunk,window", [(4, 8, 0), (5, 6, 3), (4, 8, 8), (6, 5, 12), (3, 7, 1)])
+def test_visible_pairs_match_enumeration(p, chunk, window):
+    items = (oracle.window_schedule(p, chunk, window)[0] if window > 0
+             else oracle.balanced_schedule(p)[0])
+    for it in items:
+        assert bench.visible_pairs(it, chunk, window) == _brute(it[2], it[3], chunk, window), it
+
+
+def test_causal_pair_counts():
+    assert bench.pairs_of(0, 32768) == 32768 * 32769 // 2
+    assert bench.pairs_of(1, 32768) == 32768 ** 2
