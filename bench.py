@@ -49,6 +49,8 @@ def source_digest(name: str) -> str:
     h = hashlib.sha256()
     for f in (KERNEL_SOURCES[name], "common.hpp"):
         h.update(open(os.path.join(csrc, f), "rb").read())
+    # the compiler options are part of the kernel too
+    h.update(open(os.path.join(ROOT, "long_context_exact_amd", "build.py"), "rb").read())
     return h.hexdigest()[:16]
 
 
