@@ -39,15 +39,16 @@ KERNEL_NAMES = {"fwd": "fwd_bf16_kernel", "dkdv": "dkdv_bf16_kernel", "dq": "dq_
 # fp32 inputs run the exact fp32 kernels (one wave per row, vector ALU, no MFMA)
 KERNEL_NAMES_F32 = {"fwd": "fwd_f32_kernel", "dkdv": "dkdv_f32_kernel", "dq": "dq_f32_kernel"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-KERNEL_SOURCES = {"fwd_bf16_kernel": "fwd_mfma.hip", "dkdv_bf16_kernel": "bwd_mfma.hip",
-                  "dq_bf16_kernel": "bwd_mfma.hip"}
+KERNEL_SOURCES = {"fwd_bf16_kernel": ("fwd_mfma.hip",),
+                  "dkdv_bf16_kernel": ("dkdv_mfma.hip", "bwd_common.hpp"),
+                  "dq_bf16_kernel": ("dq_mfma.hip", "bwd_common.hpp")}
 
 
 def source_digest(name: str) -> str:
     import hashlib
     csrc = os.path.join(ROOT, "long_context_exact_amd", "csrc")
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCES[name], "common.hpp"):
+    for f in KERNEL_SOURCES[name] + ("common.hpp",):
         h.update(open(os.path.join(csrc, f), "rb").read())
     # the compiler options are part of the kernel too
     h.update(open(os.path.join(ROOT, "long_context_exact_amd", "build.py"), "rb").read())

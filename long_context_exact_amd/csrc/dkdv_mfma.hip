@@ -1,0 +1,294 @@
+// dK / dV of one chunk pair on gfx950 bf16 MFMA (the key-outer half of the
+// backward; see bwd_mfma.hip for the pair of kernels and their contract).
+#include <algorithm>
+#include <cfloat>
+
+#include "bwd_common.hpp"
+
+namespace dfa {
+namespace {
+
+// ---------------------------------------------------------------- dK, dV
+// Each wave keeps its 32 keys' K rows in VGPRs (the B operand of S for the
+// whole run); the workgroup's V rows stay in LDS, Q and dO come in
+// double-buffered 32-row stages, and wave 0 stages each step's row
+// statistics (-log2 e * LSE and delta) into the same stage, so no wave
+// holds them in registers between steps.
+template <int D, int NW>
+struct DkvCfg {
+  static constexpr int NT = NW * 64;
+  static constexpr int BK = 32 * NW;            // keys per workgroup
+  static constexpr int BQ = 32;                 // query rows per step
+  static constexpr int KV_TILE = BK * D;        // elements of the K (or V) tile
+  static constexpr int KV_SEGS = KV_TILE / 512; // 1 KiB segments
+  static constexpr int Q_TILE = BQ * D;         // elements of one Q (or dO) tile
+  static constexpr int Q_SEGS = Q_TILE / 512;
+  static constexpr int STATS = 2 * BQ;           // -log2 LSE and delta of a step's rows (floats)
+  static constexpr int STAGE = 2 * Q_TILE + 2 * STATS;  // Q + dO + row statistics (16-bit units)
+  static constexpr int LDS_BYTES = (KV_TILE + 2 * STAGE) * 2;
+  static_assert(KV_SEGS % NW == 0, "key tile segments must divide over the waves");
+  static_assert(Q_SEGS % NW == 0 || NW % Q_SEGS == 0, "query segments over the waves");
+  static_assert(LDS_BYTES <= 160 * 1024, "fits gfx950 LDS");
+};
+
+template <int D, int NW, bool FULL>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DFA_BWD_OCC, DFA_BWD_OCC)))
+void dkdv_bf16_kernel(BwdArgs a) {
+  using C = DkvCfg<D, NW>;
+  extern __shared__ __align__(16) uint16_t smem_generic[];
+  lds_u16* smem = lds_base(smem_generic);
+  lds_u16* Vs = smem;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+  const int lane = tid & 63;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int half16 = (lane >> 4) & 1;
+  const int kt = blockIdx.x / a.hkv;
+  const int g = blockIdx.x % a.hkv;
+  const int64_t b = blockIdx.y;
+  const int64_t k_lo = int64_t(kt) * C::BK;
+  const int64_t wk_lo = k_lo + wave * 32;
+  const int64_t wk_hi = min(wk_lo + 32, a.len_kv);
+  const bool wave_active = wk_lo < a.len_kv;
+  const int64_t key = wk_lo + l32;
+
+  const int64_t q_rs = int64_t(a.hq) * D;
+  const int64_t kv_rs = int64_t(a.hkv) * D;
+
+  // Query rows that see at least one key of this workgroup: from the first
+  // row at or after its first key, to the last row whose window still
+  // reaches its last key.
+  int64_t i_begin = 0;
+  if (a.causal) i_begin = max<int64_t>(0, a.kv_start + k_lo - a.q_start);
+  const int64_t i_end =
+      min<int64_t>(a.len_q, a.kv_start + min<int64_t>(k_lo + C::BK, a.len_kv) - 1 + a.win - a.q_start);
+  if (i_begin >= i_end) return;  // uniform over the workgroup
+  const int qt0 = int(i_begin / C::BQ);
+  const int nq = int(cdiv(i_end, C::BQ)) - qt0;
+  const int steps = a.group * nq;
+
+  // K of this lane's key as the B operand of S (elements d = 16*st + 8*hi
+  // + e), in VGPRs for the whole loop; V rows of the workgroup in LDS.
+  bf16x8 kf[D / 16];
+  {
+    const uint16_t* kp = a.k + (b * a.len_kv + key) * kv_rs + int64_t(g) * D;
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st)
+      kf[st] = key < a.len_kv ? ld_bf16x8(kp + 16 * st + 8 * hi) : bf16x8{};
+    const uint16_t* vb = a.v + b * a.len_kv * kv_rs + int64_t(g) * D;
+    const int64_t last = a.len_kv - 1;  // rows past the chunk re-read its last key (masked)
+#pragma unroll
+    for (int i = 0; i < C::KV_SEGS / NW; ++i) {
+      const int seg = wave * (C::KV_SEGS / NW) + i;
+      tile_dma_segment<D>(Vs, seg, lane, [&](int r) {
+        return vb + min<int64_t>(k_lo + r, last) * kv_rs;
+      });
+    }
+  }
+
+  f32x16 dk_acc[D / 32], dv_acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    dk_acc[db] = f32x16{};
+    dv_acc[db] = f32x16{};
+  }
+
+  auto stage_ptr = [&](int stage) { return smem + C::KV_TILE + stage * C::STAGE; };
+  auto stage_q = [&](int it, int stage) {
+    const int h = g * a.group + it / nq;
+    const int64_t i0 = int64_t(qt0 + it % nq) * C::BQ;
+    const uint16_t* qb = a.q + b * a.len_q * q_rs + int64_t(h) * D;
+    const uint16_t* db_ = a.d_o + b * a.len_q * q_rs + int64_t(h) * D;
+    lds_u16* Qs = stage_ptr(stage);
+    lds_u16* dOs = Qs + C::Q_TILE;
+    if constexpr (FULL) {  // every row of every step is in range
+      constexpr int RPS = 512 / D;
+      for (int seg = wave; seg < 2 * C::Q_SEGS; seg += NW) {
+        if (seg < C::Q_SEGS)
+          tile_dma_segment_rows<D>(Qs, seg, lane, qb + (i0 + seg * RPS) * q_rs, uint32_t(q_rs * 2));
+        else
+          tile_dma_segment_rows<D>(dOs, seg - C::Q_SEGS, lane,
+                                   db_ + (i0 + (seg - C::Q_SEGS) * RPS) * q_rs, uint32_t(q_rs * 2));
+      }
+      return;
+    }
+    const int64_t last = a.len_q - 1;  // rows past the chunk re-read its last row (P = 0)
+    // 2 * Q_SEGS segments (Q then dO) spread over the waves
+    for (int seg = wave; seg < 2 * C::Q_SEGS; seg += NW) {
+      if (seg < C::Q_SEGS)
+        tile_dma_segment<D>(Qs, seg, lane, [&](int r) {
+          return qb + min<int64_t>(i0 + r, last) * q_rs;
+        });
+      else
+        tile_dma_segment<D>(dOs, seg - C::Q_SEGS, lane, [&](int r) {
+          return db_ + min<int64_t>(i0 + r, last) * q_rs;
+        });
+    }
+  };
+
+  // Row statistics of a step, staged by wave 0 into the step's LDS stage:
+  // lane r < 32 holds -log2(e) * LSE of row r (-inf for rows without keys or
+  // past the chunk, so that P = exp2(fma(s, c, nl)) = 0), lane 32 + r holds
+  // delta of row r.  Every wave then reads its lanes' rows from LDS.
+  static_assert(C::BQ <= 64, "one lane per row of a step");
+  float stat_l = 0.f, stat_d = 0.f;
+  auto load_stats = [&](int it) {
+    const int h = g * a.group + it / nq;
+    const int64_t row = int64_t(qt0 + it % nq) * C::BQ + lane;
+    const int64_t li = (b * a.hq + h) * a.len_q + row;
+    const bool ok = lane < C::BQ && (FULL || row < a.len_q);
+    const float x = ok ? a.lse[li] : -INFINITY;
+    // every row of a fully visible pair sees keys, so its LSE is finite
+    stat_l = (FULL || x > -INFINITY) ? -x * kLog2e : -INFINITY;
+    stat_d = ok ? a.delta[li] : 0.f;
+  };
+  auto store_stats = [&](int stage) {
+    lds_f32* st = reinterpret_cast<lds_f32*>(stage_ptr(stage) + 2 * C::Q_TILE);
+    if (lane < C::BQ) {
+      st[lane] = stat_l;
+      st[C::BQ + lane] = stat_d;
+    }
+  };
+
+  stage_q(0, 0);
+  if (wave == 0) load_stats(0);
+  wait_vmem();
+  if (wave == 0) store_stats(0);
+  __syncthreads();
+
+#pragma unroll 1
+  for (int it = 0; it < steps; ++it) {
+    if (it + 1 < steps) {  // lands while this step computes
+      stage_q(it + 1, (it + 1) & 1);
+      if (wave == 0) load_stats(it + 1);
+    }
+    const lds_u16* Qs = stage_ptr(it & 1);
+    const lds_u16* dOs = Qs + C::Q_TILE;
+    const lds_f32* stats = reinterpret_cast<const lds_f32*>(Qs + 2 * C::Q_TILE);
+    const int64_t r0 = int64_t(qt0 + it % nq) * C::BQ;  // first row of this step
+    bool any = wave_active;
+    if constexpr (!FULL) {
+      if (any && a.causal) any = a.q_start + min<int64_t>(r0 + C::BQ, a.len_q) - 1 >= a.kv_start + wk_lo;
+      if (any) any = a.q_start + r0 - (a.kv_start + wk_hi - 1) < a.win;
+    }
+    if (any) {
+      // S first, then dP: the exponentials below can run while dP's
+      // instructions are still in the matrix pipe.
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st)
+        s = mfma32(tile_row8<D>(Qs, l32, 2 * st + hi), kf[st], s);
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st)
+        dp = mfma32(tile_row8<D>(dOs, l32, 2 * st + hi), tile_row8<D>(Vs, wave * 32 + l32, 2 * st + hi), dp);
+      bool need_mask = false;
+      if constexpr (!FULL)
+        need_mask = (a.causal && a.q_start + r0 < a.kv_start + wk_hi - 1) ||
+                    (r0 + C::BQ > a.len_q) || (wk_lo + 32 > a.len_kv) ||
+                    a.q_start + r0 + C::BQ - 1 - (a.kv_start + wk_lo) >= a.win;
+      if (need_mask) {  // hidden scores -> -inf, so P = exp2(-inf) = 0 (c > 0)
+        const int64_t rmin = a.causal ? a.kv_start + key - a.q_start - r0 : INT64_MIN / 2;
+        const int64_t rmax = min<int64_t>(a.len_q - 1 - r0, a.kv_start + key + a.win - 1 - a.q_start - r0);
+        const bool key_ok = key < a.len_kv;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ri = 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (!key_ok || ri < rmin || ri > rmax) s[r] = -INFINITY;
+        }
+      }
+      // P, then dV^T += dO^T P; dS is formed while those instructions run.
+      // This lane's rows are 8 * (r / 4) + 4 * hi + r % 4.
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 nl = *reinterpret_cast<const DFA_LDS f32x4*>(stats + 8 * r4 + 4 * hi);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[4 * r4 + e] = exp2_fast(fmaf(s[4 * r4 + e], a.c, nl[e]));
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        bf16x8 pb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(s[8 * j + e]);
+        const int t0 = 16 * j + 4 * hi;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const int c0 = 32 * db + 16 * half16;
+          const bf16x8 ta = cat4(tile_tr4<D>(dOs, t0, c0, lane), tile_tr4<D>(dOs, t0 + 8, c0, lane));
+          dv_acc[db] = mfma32(ta, pb, dv_acc[db]);
+        }
+      }
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 dl = *reinterpret_cast<const DFA_LDS f32x4*>(stats + C::BQ + 8 * r4 + 4 * hi);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dp[4 * r4 + e] = s[4 * r4 + e] * (dp[4 * r4 + e] - dl[e]);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        bf16x8 sb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sb[e] = static_cast<__bf16>(dp[8 * j + e]);
+        const int t0 = 16 * j + 4 * hi;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const int c0 = 32 * db + 16 * half16;
+          const bf16x8 ua = cat4(tile_tr4<D>(Qs, t0, c0, lane), tile_tr4<D>(Qs, t0 + 8, c0, lane));
+          dk_acc[db] = mfma32(ua, sb, dk_acc[db]);
+        }
+      }
+    }
+    // The next stage this wave staged (and, for wave 0, the next step's row
+    // statistics) must land before the barrier.
+    if (it + 1 < steps) {
+      wait_vmem();
+      if (wave == 0) store_stats((it + 1) & 1);
+    }
+    __syncthreads();
+  }
+
+  if (!wave_active || key >= a.len_kv) return;
+  float* dkr = a.dk + (b * a.len_kv + key) * kv_rs + int64_t(g) * D;
+  float* dvr = a.dv + (b * a.len_kv + key) * kv_rs + int64_t(g) * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d = 32 * db + 8 * r4 + 4 * hi;
+      f32x4 xk = *reinterpret_cast<f32x4*>(dkr + d);
+      f32x4 xv = *reinterpret_cast<f32x4*>(dvr + d);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        xk[e] += a.scale * dk_acc[db][4 * r4 + e];
+        xv[e] += dv_acc[db][4 * r4 + e];
+      }
+      *reinterpret_cast<f32x4*>(dkr + d) = xk;
+      *reinterpret_cast<f32x4*>(dvr + d) = xv;
+    }
+}
+
+constexpr int kDkvNW = 8;
+
+template <int D>
+dfa_status launch_dkdv(const dfa_attn_desc& d, BwdArgs a, hipStream_t s) {
+  using C = DkvCfg<D, kDkvNW>;
+  dim3 grid(unsigned(cdiv(d.len_kv, C::BK)) * unsigned(d.heads_kv), unsigned(d.batch));
+  auto go = [&](auto kern) {
+    const dfa_status st = allow_lds(kern, C::LDS_BYTES, "dkdv_bf16_kernel");
+    if (st != DFA_OK) return st;
+    hipLaunchKernelGGL(kern, grid, dim3(C::NT), C::LDS_BYTES, s, a);
+    return check_launch("dkdv_bf16_kernel");
+  };
+  if (pair_is_full(d, C::BK) && d.len_q % C::BQ == 0)
+    return go(dkdv_bf16_kernel<D, kDkvNW, true>);
+  return go(dkdv_bf16_kernel<D, kDkvNW, false>);
+}
+
+}  // namespace
+
+dfa_status launch_dkdv_bf16(const dfa_attn_desc& d, const BwdArgs& a, hipStream_t s) {
+  if (d.head_dim == 128) return launch_dkdv<128>(d, a, s);
+  return launch_dkdv<64>(d, a, s);
+}
+
+}  // namespace dfa

@@ -1,0 +1,262 @@
+// dQ of one chunk pair on gfx950 bf16 MFMA (the query-outer half of the
+// backward; see bwd_mfma.hip for the pair of kernels and their contract).
+#include <algorithm>
+#include <cfloat>
+
+#include "bwd_common.hpp"
+
+namespace dfa {
+namespace {
+
+// ---------------------------------------------------------------- dQ
+template <int D, int NW, int HPW, int BN>
+struct DqCfg {
+  static constexpr int NT = NW * 64;
+  static constexpr int BM = 32 * (NW / HPW);
+  static constexpr int NSB = BN / 32;
+  static constexpr int TILE = BN * D;
+  static constexpr int SEGS = TILE / 512;
+  static constexpr int STAGE = 2 * TILE;  // K tile + V tile (elements)
+  static constexpr int LDS_BYTES = 2 * STAGE * 2;
+  static_assert(SEGS % NW == 0, "key tile segments must divide over the waves");
+};
+
+template <int D, int NW, int HPW, int BN, bool FULL>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DFA_BWD_OCC, DFA_BWD_OCC)))
+void dq_bf16_kernel(BwdArgs a) {
+  using C = DqCfg<D, NW, HPW, BN>;
+  extern __shared__ __align__(16) uint16_t smem_generic[];
+  lds_u16* smem = lds_base(smem_generic);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+  const int lane = tid & 63;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int half16 = (lane >> 4) & 1;
+  const int bid = blockIdx.x;
+  const int qt = a.n_tiles - 1 - bid / a.n_hgroups;
+  const int hg = bid % a.n_hgroups;
+  const int64_t b = blockIdx.y;
+  const int h = hg * HPW + wave % HPW;
+  const int g = (hg * HPW) / a.group;
+  const int64_t q_lo = int64_t(qt) * C::BM;
+  const int64_t w_lo = q_lo + (wave / HPW) * 32;
+  const int64_t q_hi = min(q_lo + C::BM, a.len_q);
+  const int64_t w_hi = min(w_lo + 32, a.len_q);
+  const bool wave_active = w_lo < a.len_q;
+  const int64_t row = w_lo + l32;
+
+  const int64_t q_rs = int64_t(a.hq) * D;
+  const int64_t kv_rs = int64_t(a.hkv) * D;
+  const uint16_t* kbase = a.k + b * a.len_kv * kv_rs + int64_t(g) * D;
+  const uint16_t* vbase = a.v + b * a.len_kv * kv_rs + int64_t(g) * D;
+
+  bf16x8 qf[D / 16], df[D / 16];
+  float lse2 = INFINITY, dl = 0.f;
+  {
+    const int64_t off = (b * a.len_q + row) * q_rs + int64_t(h) * D;
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+      qf[st] = row < a.len_q ? ld_bf16x8(a.q + off + 16 * st + 8 * hi) : bf16x8{};
+      df[st] = row < a.len_q ? ld_bf16x8(a.d_o + off + 16 * st + 8 * hi) : bf16x8{};
+    }
+    if (row < a.len_q) {
+      const int64_t li = (b * a.hq + h) * a.len_q + row;
+      lse2 = lse2_of(a.lse[li]);
+      dl = a.delta[li];
+    }
+  }
+
+  int kt_end = a.n_ktiles;
+  if (a.causal) {
+    const int64_t lim = a.q_start + (q_hi - 1) - a.kv_start;
+    kt_end = lim < 0 ? 0 : int(min<int64_t>(a.n_ktiles, lim / BN + 1));
+  }
+  int kt_begin = 0;  // first key tile inside the window of the tile's first row
+  {
+    const int64_t lo = a.q_start + q_lo - a.win + 1 - a.kv_start;
+    if (lo > 0) kt_begin = lo >= a.len_kv ? a.n_ktiles : int(lo / BN);
+  }
+  if (kt_begin >= kt_end) return;  // uniform: no key visible to any row here
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+
+  auto stage_tile = [&](int kt, int stage) {
+    lds_u16* Ks = smem + stage * C::STAGE;
+    lds_u16* Vs = Ks + C::TILE;
+    const int64_t key0 = int64_t(kt) * BN;
+    if constexpr (FULL) {  // every row of every tile is in range
+      constexpr int RPS = 512 / D;
+#pragma unroll
+      for (int i = 0; i < C::SEGS / NW; ++i) {
+        const int seg = wave * (C::SEGS / NW) + i;
+        const int64_t r0 = (key0 + seg * RPS) * kv_rs;
+        tile_dma_segment_rows<D>(Ks, seg, lane, kbase + r0, uint32_t(kv_rs * 2));
+        tile_dma_segment_rows<D>(Vs, seg, lane, vbase + r0, uint32_t(kv_rs * 2));
+      }
+      return;
+    }
+    const int64_t last = a.len_kv - 1;  // rows past the chunk re-read its last key (masked)
+#pragma unroll
+    for (int i = 0; i < C::SEGS / NW; ++i) {
+      const int seg = wave * (C::SEGS / NW) + i;
+      tile_dma_segment<D>(Ks, seg, lane, [&](int r) {
+        return kbase + min<int64_t>(key0 + r, last) * kv_rs;
+      });
+      tile_dma_segment<D>(Vs, seg, lane, [&](int r) {
+        return vbase + min<int64_t>(key0 + r, last) * kv_rs;
+      });
+    }
+  };
+  // S^T = K Q^T and dP^T = V dO^T of one 32-key sub-block (lane = query row).
+  auto sdp = [&](const lds_u16* Ks, const lds_u16* Vs, int kb, f32x16& s, f32x16& dp) {
+    s = f32x16{};
+    dp = f32x16{};
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+      s = mfma32(tile_row8<D>(Ks, kb * 32 + l32, 2 * st + hi), qf[st], s);
+      dp = mfma32(tile_row8<D>(Vs, kb * 32 + l32, 2 * st + hi), df[st], dp);
+    }
+  };
+  // dS^T = P^T (dP^T - delta) (hidden scores already -inf), dQ^T += K^T dS^T.
+  auto update = [&](const lds_u16* Ks, int kb, const f32x16& s, f32x16& dp) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = exp2_fast(fmaf(s[r], a.c, -lse2));
+      dp[r] = p * (dp[r] - dl);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      bf16x8 sb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sb[e] = static_cast<__bf16>(dp[8 * j + e]);
+      const int t0 = kb * 32 + 16 * j + 4 * hi;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int c0 = 32 * db + 16 * half16;
+        const bf16x8 ta = cat4(tile_tr4<D>(Ks, t0, c0, lane), tile_tr4<D>(Ks, t0 + 8, c0, lane));
+        acc[db] = mfma32(ta, sb, acc[db]);
+      }
+    }
+  };
+
+  stage_tile(kt_begin, kt_begin & 1);
+  wait_vmem();
+  __syncthreads();
+
+  for (int kt = kt_begin; kt < kt_end; ++kt) {
+    if (kt + 1 < kt_end) stage_tile(kt + 1, (kt + 1) & 1);  // lands while this tile computes
+    const lds_u16* Ks = smem + (kt & 1) * C::STAGE;
+    const lds_u16* Vs = Ks + C::TILE;
+    const int64_t key0 = int64_t(kt) * BN;
+    if constexpr (FULL) {
+      if (wave_active) {
+        f32x16 s, dp;
+        sdp(Ks, Vs, 0, s, dp);
+#pragma unroll 1
+        for (int kb = 0; kb < C::NSB - 1; ++kb) {
+          f32x16 s2, dp2;
+          sdp(Ks, Vs, kb + 1, s2, dp2);  // independent of the vector work below
+          update(Ks, kb, s, dp);
+          s = s2;
+          dp = dp2;
+        }
+        update(Ks, C::NSB - 1, s, dp);
+      }
+    } else {
+      int nsb = 0, kb0 = 0;
+      if (wave_active) {
+        int64_t vis_last = a.len_kv - 1 - key0;
+        if (a.causal) vis_last = min(vis_last, a.q_start + (w_hi - 1) - a.kv_start - key0);
+        nsb = vis_last < 0 ? 0 : int(min<int64_t>(C::NSB, vis_last / 32 + 1));
+        const int64_t vis_first = a.q_start + w_lo - a.win + 1 - a.kv_start - key0;
+        if (vis_first > 0) kb0 = int(min<int64_t>(C::NSB, vis_first / 32));
+      }
+#pragma unroll 1
+      for (int kb = kb0; kb < nsb; ++kb) {
+        f32x16 s, dp;
+        sdp(Ks, Vs, kb, s, dp);
+        const int64_t kfirst = key0 + kb * 32;
+        if ((a.causal && a.kv_start + kfirst + 31 > a.q_start + w_lo) || kfirst + 32 > a.len_kv ||
+            a.q_start + (w_hi - 1) - (a.kv_start + kfirst) >= a.win) {
+          // hidden scores -> -inf, so P = exp2(-inf) = 0 (c > 0)
+          int64_t vlim = a.len_kv - 1 - kfirst;
+          if (a.causal) vlim = min(vlim, a.q_start + row - a.kv_start - kfirst);
+          const int64_t vmin = a.q_start + row - a.win + 1 - a.kv_start - kfirst;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int off = 8 * (r >> 2) + 4 * hi + (r & 3);
+            if (off > vlim || off < vmin) s[r] = -INFINITY;
+          }
+        }
+        update(Ks, kb, s, dp);
+      }
+    }
+    wait_vmem();  // the next tile's segments this wave staged have landed
+    __syncthreads();
+  }
+
+  if (!wave_active || row >= a.len_q) return;
+  float* out = a.dq + (b * a.len_q + row) * q_rs + int64_t(h) * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d = 32 * db + 8 * r4 + 4 * hi;
+      f32x4 x = *reinterpret_cast<f32x4*>(out + d);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] += a.scale * acc[db][4 * r4 + e];
+      *reinterpret_cast<f32x4*>(out + d) = x;
+    }
+}
+
+#ifndef DFA_DQ_BN
+#define DFA_DQ_BN 64
+#endif
+constexpr int kDqBN = DFA_DQ_BN;
+
+int dq_hpw(int group) {
+  if (group % 8 == 0) return 8;
+  if (group % 4 == 0) return 4;
+  if (group % 2 == 0) return 2;
+  return 1;
+}
+
+template <int D, int HPW>
+dfa_status launch_dq(const dfa_attn_desc& d, BwdArgs a, hipStream_t s) {
+  constexpr int NW = 8;
+  using C = DqCfg<D, NW, HPW, kDqBN>;
+  a.n_tiles = int(cdiv(d.len_q, C::BM));
+  a.n_hgroups = d.heads_q / HPW;
+  a.n_ktiles = int(cdiv(d.len_kv, kDqBN));
+  dim3 grid(unsigned(a.n_tiles) * unsigned(a.n_hgroups), unsigned(d.batch));
+  auto go = [&](auto kern) {
+    const dfa_status st = allow_lds(kern, C::LDS_BYTES, "dq_bf16_kernel");
+    if (st != DFA_OK) return st;
+    hipLaunchKernelGGL(kern, grid, dim3(C::NT), C::LDS_BYTES, s, a);
+    return check_launch("dq_bf16_kernel");
+  };
+  if (pair_is_full(d, kDqBN)) return go(dq_bf16_kernel<D, NW, HPW, kDqBN, true>);
+  return go(dq_bf16_kernel<D, NW, HPW, kDqBN, false>);
+}
+
+template <int D>
+dfa_status launch_dq_d(const dfa_attn_desc& d, const BwdArgs& a, hipStream_t s) {
+  switch (dq_hpw(a.group)) {
+    case 8: return launch_dq<D, 8>(d, a, s);
+    case 4: return launch_dq<D, 4>(d, a, s);
+    case 2: return launch_dq<D, 2>(d, a, s);
+    default: return launch_dq<D, 1>(d, a, s);
+  }
+}
+
+}  // namespace
+
+dfa_status launch_dq_bf16(const dfa_attn_desc& d, const BwdArgs& a, hipStream_t s) {
+  if (d.head_dim == 128) return launch_dq_d<128>(d, a, s);
+  return launch_dq_d<64>(d, a, s);
+}
+
+}  // namespace dfa
