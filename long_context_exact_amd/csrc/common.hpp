@@ -122,12 +122,38 @@ __device__ __forceinline__ bf16x4 tile_tr4(const lds_u16* t, int row0, int col0,
   return __builtin_bit_cast(bf16x4, r);
 }
 
-// Direct global -> LDS staging of a swizzled tile (global_load_lds_dwordx4):
-// lane i of a wave writes the 16 bytes at LDS byte address M0 + 16 * i, so a
-// wave fills one 1 KiB segment per instruction; to land chunk c of row r at
-// its swizzled slot, the lane whose slot is (r, p) loads the global chunk
-// c = p ^ g(r).  `seg` is the segment index inside the tile; `row_ptr(r)`
-// gives the global address of the tile's row r (already clamped in range).
+// Direct global -> LDS transfer of 16 bytes per lane (global_load_lds_dwordx4):
+// lane i writes the 16 bytes at LDS byte address M0 + 16 * i.  Issued from
+// inline assembly on purpose: when the compiler sees these transfers it makes
+// every later LDS read it cannot prove disjoint from them (the transposed
+// reads) wait for all of them, which stalls each tile loop on the prefetch of
+// its next tile.  Callers instead order the transfers themselves with
+// wait_vmem() and a barrier before the staged tile is read.  M0 is set
+// inside each statement (1 wait state before the transfer reads it); no other
+// code in these kernels uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const void* src, const void DFA_LDS* dst_wave) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst_wave)));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(m0), "v"(src) : "memory", "m0");
+}
+// Same with a wave-uniform base address and a 32-bit per-lane byte offset.
+__device__ __forceinline__ void lds_dma16_off(const void* base, uint32_t off,
+                                              const void DFA_LDS* dst_wave) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst_wave)));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(m0), "v"(off), "s"(base) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Staging of a swizzled tile: a wave fills one 1 KiB segment per transfer; to
+// land chunk c of row r at its swizzled slot, the lane whose slot is (r, p)
+// loads the global chunk c = p ^ g(r).  `seg` is the segment index inside the
+// tile; `row_ptr(r)` gives the global address of the tile's row r (already
+// clamped in range).
 template <int D, typename RowPtr>
 __device__ __forceinline__ void tile_dma_segment(lds_u16* tile, int seg, int lane, RowPtr row_ptr) {
   constexpr int ROWS_PER_SEG = 512 / D;    // 1 KiB / (2 bytes * D)
@@ -136,9 +162,7 @@ __device__ __forceinline__ void tile_dma_segment(lds_u16* tile, int seg, int lan
   const int phys = lane % CHUNKS;
   // logical chunk whose swizzled slot is `phys` (g is an involution partner)
   const int logical = (swz<D>(row, phys) - row * D) >> 3;
-  const uint16_t* src = row_ptr(row) + 8 * logical;
-  typedef DFA_LDS void lds_void;
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)(tile + seg * 512), 16, 0, 0);
+  lds_dma16(row_ptr(row) + 8 * logical, tile + seg * 512);
 }
 
 // Same staging when the segment's rows are consecutive rows of one tensor,
@@ -153,9 +177,7 @@ __device__ __forceinline__ void tile_dma_segment_rows(lds_u16* tile, int seg, in
   const int row = seg * ROWS_PER_SEG + r_in;
   const int logical = (swz<D>(row, lane % CHUNKS) - row * D) >> 3;
   const uint32_t off = uint32_t(r_in) * row_bytes + uint32_t(logical) * 16u;
-  typedef DFA_LDS void lds_void;
-  __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(seg_base) + off,
-                                   (lds_void*)(tile + seg * 512), 16, 0, 0);
+  lds_dma16_off(seg_base, off, tile + seg * 512);
 }
 
 // Wait for this wave's outstanding global loads (including LDS-direct ones).

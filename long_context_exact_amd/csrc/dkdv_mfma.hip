@@ -130,24 +130,30 @@ void dkdv_bf16_kernel(BwdArgs a) {
   // Row statistics of a step, staged by wave 0 into the step's LDS stage:
   // lane r < 32 holds -log2(e) * LSE of row r (-inf for rows without keys or
   // past the chunk, so that P = exp2(fma(s, c, nl)) = 0), lane 32 + r holds
-  // delta of row r.  Every wave then reads its lanes' rows from LDS.
+  // delta of row r.  Every wave then reads its lanes' rows from LDS.  The
+  // loads are issued with the next stage and consumed only after the wait
+  // that ends the step: consuming them at once would hold wave 0, and with
+  // it the step's barrier, behind that stage's transfer.
   static_assert(C::BQ <= 64, "one lane per row of a step");
-  float stat_l = 0.f, stat_d = 0.f;
+  float raw_l = 0.f, raw_d = 0.f;
+  bool raw_ok = false;
   auto load_stats = [&](int it) {
     const int h = g * a.group + it / nq;
     const int64_t row = int64_t(qt0 + it % nq) * C::BQ + lane;
-    const int64_t li = (b * a.hq + h) * a.len_q + row;
-    const bool ok = lane < C::BQ && (FULL || row < a.len_q);
-    const float x = ok ? a.lse[li] : -INFINITY;
-    // every row of a fully visible pair sees keys, so its LSE is finite
-    stat_l = (FULL || x > -INFINITY) ? -x * kLog2e : -INFINITY;
-    stat_d = ok ? a.delta[li] : 0.f;
+    raw_ok = lane < C::BQ && (FULL || row < a.len_q);
+    const int64_t li = (b * a.hq + h) * a.len_q + min<int64_t>(row, a.len_q - 1);
+    raw_l = a.lse[li];
+    raw_d = a.delta[li];
   };
   auto store_stats = [&](int stage) {
+    const float x = raw_ok ? raw_l : -INFINITY;
+    // every row of a fully visible pair sees keys, so its LSE is finite
+    const float nl = (FULL || x > -INFINITY) ? -x * kLog2e : -INFINITY;
+    const float dl = raw_ok ? raw_d : 0.f;
     lds_f32* st = reinterpret_cast<lds_f32*>(stage_ptr(stage) + 2 * C::Q_TILE);
     if (lane < C::BQ) {
-      st[lane] = stat_l;
-      st[C::BQ + lane] = stat_d;
+      st[lane] = nl;
+      st[C::BQ + lane] = dl;
     }
   };
 
