@@ -133,15 +133,7 @@ __device__ __forceinline__ bf16x4 tile_tr4(const lds_u16* t, int row0, int col0,
 // code in these kernels uses M0.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void lds_dma16(const void* src, const void DFA_LDS* dst_wave) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst_wave)));
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(m0), "v"(src) : "memory", "m0");
-}
-// Same with a wave-uniform base address and a 32-bit per-lane byte offset.
-__device__ __forceinline__ void lds_dma16_off(const void* base, uint32_t off,
-                                              const void DFA_LDS* dst_wave) {
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t off, const void DFA_LDS* dst_wave) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst_wave)));
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
@@ -149,35 +141,22 @@ __device__ __forceinline__ void lds_dma16_off(const void* base, uint32_t off,
 }
 #pragma clang diagnostic pop
 
-// Staging of a swizzled tile: a wave fills one 1 KiB segment per transfer; to
-// land chunk c of row r at its swizzled slot, the lane whose slot is (r, p)
-// loads the global chunk c = p ^ g(r).  `seg` is the segment index inside the
-// tile; `row_ptr(r)` gives the global address of the tile's row r (already
-// clamped in range).
-template <int D, typename RowPtr>
-__device__ __forceinline__ void tile_dma_segment(lds_u16* tile, int seg, int lane, RowPtr row_ptr) {
-  constexpr int ROWS_PER_SEG = 512 / D;    // 1 KiB / (2 bytes * D)
+// Staging of segment `seg` (1 KiB) of a swizzled tile: row r of the tile is
+// read from tile_base + r * row_bytes (tile_base wave-uniform, so each lane
+// adds only a 32-bit offset), and rows past `last_row` re-read row last_row
+// (ragged ends; those rows are masked by the caller).  To land chunk c of row
+// r at its swizzled slot, the lane whose slot is (r, p) loads the global
+// chunk c = p ^ g(r).
+template <int D>
+__device__ __forceinline__ void tile_dma_rows(lds_u16* tile, int seg, int lane, const uint16_t* tile_base,
+                                              uint32_t row_bytes, int last_row) {
+  constexpr int ROWS_PER_SEG = 512 / D;  // 1 KiB / (2 bytes * D)
   constexpr int CHUNKS = D / 8;
   const int row = seg * ROWS_PER_SEG + lane / CHUNKS;
-  const int phys = lane % CHUNKS;
-  // logical chunk whose swizzled slot is `phys` (g is an involution partner)
-  const int logical = (swz<D>(row, phys) - row * D) >> 3;
-  lds_dma16(row_ptr(row) + 8 * logical, tile + seg * 512);
-}
-
-// Same staging when the segment's rows are consecutive rows of one tensor,
-// all in range: `seg_base` (wave-uniform) is the segment's first row and
-// rows are `row_bytes` apart, so each lane adds only a 32-bit offset.
-template <int D>
-__device__ __forceinline__ void tile_dma_segment_rows(lds_u16* tile, int seg, int lane,
-                                                      const uint16_t* seg_base, uint32_t row_bytes) {
-  constexpr int ROWS_PER_SEG = 512 / D;
-  constexpr int CHUNKS = D / 8;
-  const int r_in = lane / CHUNKS;
-  const int row = seg * ROWS_PER_SEG + r_in;
+  // logical chunk whose swizzled slot is lane % CHUNKS (g is an involution partner)
   const int logical = (swz<D>(row, lane % CHUNKS) - row * D) >> 3;
-  const uint32_t off = uint32_t(r_in) * row_bytes + uint32_t(logical) * 16u;
-  lds_dma16_off(seg_base, off, tile + seg * 512);
+  const uint32_t off = uint32_t(min(row, last_row)) * row_bytes + uint32_t(logical) * 16u;
+  lds_dma16(tile_base, off, tile + seg * 512);
 }
 
 // Wait for this wave's outstanding global loads (including LDS-direct ones).
@@ -203,5 +182,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 dfa_status check_launch(const char* what);
 
 __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// A 64-bit offset clamped into [-2^30, 2^30]: mask bounds compared against
+// in-tile offsets (< 2^8) keep their meaning and become 32-bit compares.
+__device__ __forceinline__ int clamp_off(int64_t x) {
+  return static_cast<int>(max<int64_t>(-(int64_t(1) << 30), min<int64_t>(x, int64_t(1) << 30)));
+}
 
 }  // namespace dfa

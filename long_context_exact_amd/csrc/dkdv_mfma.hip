@@ -27,7 +27,7 @@ struct DkvCfg {
   static constexpr int STAGE = 2 * Q_TILE + 2 * STATS;  // Q + dO + row statistics (16-bit units)
   static constexpr int LDS_BYTES = (KV_TILE + 2 * STAGE) * 2;
   static_assert(KV_SEGS % NW == 0, "key tile segments must divide over the waves");
-  static_assert(Q_SEGS % NW == 0 || NW % Q_SEGS == 0, "query segments over the waves");
+  static_assert((2 * Q_SEGS) % NW == 0, "Q and dO segments divide over the waves");
   static_assert(LDS_BYTES <= 160 * 1024, "fits gfx950 LDS");
 };
 
@@ -77,13 +77,12 @@ void dkdv_bf16_kernel(BwdArgs a) {
     for (int st = 0; st < D / 16; ++st)
       kf[st] = key < a.len_kv ? ld_bf16x8(kp + 16 * st + 8 * hi) : bf16x8{};
     const uint16_t* vb = a.v + b * a.len_kv * kv_rs + int64_t(g) * D;
-    const int64_t last = a.len_kv - 1;  // rows past the chunk re-read its last key (masked)
+    // rows past the chunk re-read its last key (masked)
+    const int last_row = int(min<int64_t>(a.len_kv - 1 - k_lo, C::BK - 1));
 #pragma unroll
     for (int i = 0; i < C::KV_SEGS / NW; ++i) {
       const int seg = wave * (C::KV_SEGS / NW) + i;
-      tile_dma_segment<D>(Vs, seg, lane, [&](int r) {
-        return vb + min<int64_t>(k_lo + r, last) * kv_rs;
-      });
+      tile_dma_rows<D>(Vs, seg, lane, vb + k_lo * kv_rs, uint32_t(kv_rs * 2), last_row);
     }
   }
 
@@ -102,28 +101,20 @@ void dkdv_bf16_kernel(BwdArgs a) {
     const uint16_t* db_ = a.d_o + b * a.len_q * q_rs + int64_t(h) * D;
     lds_u16* Qs = stage_ptr(stage);
     lds_u16* dOs = Qs + C::Q_TILE;
-    if constexpr (FULL) {  // every row of every step is in range
-      constexpr int RPS = 512 / D;
-      for (int seg = wave; seg < 2 * C::Q_SEGS; seg += NW) {
-        if (seg < C::Q_SEGS)
-          tile_dma_segment_rows<D>(Qs, seg, lane, qb + (i0 + seg * RPS) * q_rs, uint32_t(q_rs * 2));
-        else
-          tile_dma_segment_rows<D>(dOs, seg - C::Q_SEGS, lane,
-                                   db_ + (i0 + (seg - C::Q_SEGS) * RPS) * q_rs, uint32_t(q_rs * 2));
-      }
-      return;
-    }
-    const int64_t last = a.len_q - 1;  // rows past the chunk re-read its last row (P = 0)
+    // rows past the chunk re-read its last row (their P is 0)
+    const int last_row = FULL ? C::BQ - 1 : int(min<int64_t>(a.len_q - 1 - i0, C::BQ - 1));
+    // The lane's staging offsets are recomputed every step (a few VALU ops)
+    // rather than hoisted out of the loop, where they would hold registers.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
     // 2 * Q_SEGS segments (Q then dO) spread over the waves
-    for (int seg = wave; seg < 2 * C::Q_SEGS; seg += NW) {
+#pragma unroll
+    for (int i = 0; i < 2 * C::Q_SEGS / NW; ++i) {
+      const int seg = wave + i * NW;
       if (seg < C::Q_SEGS)
-        tile_dma_segment<D>(Qs, seg, lane, [&](int r) {
-          return qb + min<int64_t>(i0 + r, last) * q_rs;
-        });
+        tile_dma_rows<D>(Qs, seg, ln, qb + i0 * q_rs, uint32_t(q_rs * 2), last_row);
       else
-        tile_dma_segment<D>(dOs, seg - C::Q_SEGS, lane, [&](int r) {
-          return db_ + min<int64_t>(i0 + r, last) * q_rs;
-        });
+        tile_dma_rows<D>(dOs, seg - C::Q_SEGS, ln, db_ + i0 * q_rs, uint32_t(q_rs * 2), last_row);
     }
   };
 
@@ -194,9 +185,13 @@ void dkdv_bf16_kernel(BwdArgs a) {
                     (r0 + C::BQ > a.len_q) || (wk_lo + 32 > a.len_kv) ||
                     a.q_start + r0 + C::BQ - 1 - (a.kv_start + wk_lo) >= a.win;
       if (need_mask) {  // hidden scores -> -inf, so P = exp2(-inf) = 0 (c > 0)
-        const int64_t rmin = a.causal ? a.kv_start + key - a.q_start - r0 : INT64_MIN / 2;
-        const int64_t rmax = min<int64_t>(a.len_q - 1 - r0, a.kv_start + key + a.win - 1 - a.q_start - r0);
-        const bool key_ok = key < a.len_kv;
+        // wave-uniform bounds for the wave's first key, then this lane's key
+        // offset l32: row ri of the step sees the key iff rmin <= ri <= rmax
+        const int rmin0 = a.causal ? clamp_off(a.kv_start + wk_lo - a.q_start - r0) : -(1 << 30);
+        const int rmax0 = clamp_off(a.kv_start + wk_lo + a.win - 1 - a.q_start - r0);
+        const int rmin = rmin0 + l32;
+        const int rmax = min(clamp_off(a.len_q - 1 - r0), rmax0 + l32);
+        const bool key_ok = l32 < clamp_off(a.len_kv - wk_lo);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int ri = 8 * (r >> 2) + 4 * hi + (r & 3);

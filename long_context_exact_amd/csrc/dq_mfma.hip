@@ -87,27 +87,15 @@ void dq_bf16_kernel(BwdArgs a) {
     lds_u16* Ks = smem + stage * C::STAGE;
     lds_u16* Vs = Ks + C::TILE;
     const int64_t key0 = int64_t(kt) * BN;
-    if constexpr (FULL) {  // every row of every tile is in range
-      constexpr int RPS = 512 / D;
-#pragma unroll
-      for (int i = 0; i < C::SEGS / NW; ++i) {
-        const int seg = wave * (C::SEGS / NW) + i;
-        const int64_t r0 = (key0 + seg * RPS) * kv_rs;
-        tile_dma_segment_rows<D>(Ks, seg, lane, kbase + r0, uint32_t(kv_rs * 2));
-        tile_dma_segment_rows<D>(Vs, seg, lane, vbase + r0, uint32_t(kv_rs * 2));
-      }
-      return;
-    }
-    const int64_t last = a.len_kv - 1;  // rows past the chunk re-read its last key (masked)
+    // rows past the chunk re-read its last key (their scores are masked)
+    const int last_row = FULL ? BN - 1 : int(min<int64_t>(a.len_kv - 1 - key0, BN - 1));
+    const uint16_t* kt_base = kbase + key0 * kv_rs;
+    const uint16_t* vt_base = vbase + key0 * kv_rs;
 #pragma unroll
     for (int i = 0; i < C::SEGS / NW; ++i) {
       const int seg = wave * (C::SEGS / NW) + i;
-      tile_dma_segment<D>(Ks, seg, lane, [&](int r) {
-        return kbase + min<int64_t>(key0 + r, last) * kv_rs;
-      });
-      tile_dma_segment<D>(Vs, seg, lane, [&](int r) {
-        return vbase + min<int64_t>(key0 + r, last) * kv_rs;
-      });
+      tile_dma_rows<D>(Ks, seg, lane, kt_base, uint32_t(kv_rs * 2), last_row);
+      tile_dma_rows<D>(Vs, seg, lane, vt_base, uint32_t(kv_rs * 2), last_row);
     }
   };
   // S^T = K Q^T and dP^T = V dO^T of one 32-key sub-block (lane = query row).
@@ -182,9 +170,10 @@ void dq_bf16_kernel(BwdArgs a) {
         if ((a.causal && a.kv_start + kfirst + 31 > a.q_start + w_lo) || kfirst + 32 > a.len_kv ||
             a.q_start + (w_hi - 1) - (a.kv_start + kfirst) >= a.win) {
           // hidden scores -> -inf, so P = exp2(-inf) = 0 (c > 0)
-          int64_t vlim = a.len_kv - 1 - kfirst;
-          if (a.causal) vlim = min(vlim, a.q_start + row - a.kv_start - kfirst);
-          const int64_t vmin = a.q_start + row - a.win + 1 - a.kv_start - kfirst;
+          int64_t vlim64 = a.len_kv - 1 - kfirst;
+          if (a.causal) vlim64 = min(vlim64, a.q_start + row - a.kv_start - kfirst);
+          const int vlim = clamp_off(vlim64);
+          const int vmin = clamp_off(a.q_start + row - a.win + 1 - a.kv_start - kfirst);
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int off = 8 * (r >> 2) + 4 * hi + (r & 3);
