@@ -3,13 +3,17 @@ chunked path through the C ABI, and the tolerance checks.
 
 Tolerances (float64 oracle as the truth):
   fp32 inputs: max |err| <= 1e-5 on O, LSE, dQ, dK, dV.
-  bf16 inputs, fp32 accumulation: O max |err| <= 1e-2; LSE relative <= 1e-3;
+  bf16 inputs, fp32 accumulation: O max |err| <= 1e-2 (an O delivered in
+  bf16 is allowed, on top, the rounding of the exact value to bf16: half a
+  bf16 spacing, 2**(e - 8) for |x| in [2**e, 2**(e + 1))); LSE relative <= 1e-3;
   dQ, dK, dV relative Frobenius <= 2e-2; plus an internal guard of
   relative Frobenius <= 2e-2 on O (O shrinks like 1/sqrt(prefix) at long
   contexts, where 1e-2 absolute would be loose).
 """
 
 from __future__ import annotations
+
+import zlib
 
 import numpy as np
 import torch
@@ -26,6 +30,18 @@ def rand(rng, shape, dtype, scale=1.0):
     return bf16_round(x) if dtype == "bf16" else x
 
 
+def case_seed(case) -> int:
+    """A seed that is the same in every process (Python's hash of strings is not)."""
+    return zlib.crc32(repr(case).encode())
+
+
+def bf16_half_spacing(x: np.ndarray) -> np.ndarray:
+    """Half the gap between neighbouring bf16 values at |x| (0 at x = 0)."""
+    ax = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    return np.where(ax > 0, np.exp2(e - 8), 0.0)
+
+
 def to_dev(x: np.ndarray, dtype: str) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(x)).to(DEV).to(TD[dtype])
 
@@ -39,12 +55,18 @@ def rel_fro(a, b):
     return float(np.linalg.norm(a - b) / (den if den > 0 else 1.0))
 
 
-def check_o(o, ref, dtype, what="O"):
+def check_o(o, ref, dtype, what="O", stored_bf16=False):
+    """`stored_bf16`: o is the output as delivered in bf16, so each element
+    may also differ from the exact value by the rounding to bf16."""
     err = float(np.max(np.abs(o - ref))) if o.size else 0.0
     if dtype == "f32":
         assert err <= 1e-5, f"{what}: max abs err {err}"
     else:
-        assert err <= 1e-2, f"{what}: max abs err {err}"
+        if stored_bf16 and o.size:
+            excess = float(np.max(np.abs(o - ref) - bf16_half_spacing(ref)))
+            assert excess <= 1e-2, f"{what}: max abs err {err} ({excess} beyond bf16 rounding)"
+        else:
+            assert err <= 1e-2, f"{what}: max abs err {err}"
         assert rel_fro(o, ref) <= 2e-2, f"{what}: rel fro {rel_fro(o, ref)}"
 
 

@@ -43,7 +43,7 @@ def test_autograd_function_matches_oracle(p, c, hq, hkv, d, window):
     o = A.chunked_attention(tq, tk, tv, att)
     o.backward(torch.from_numpy(do).to(DEV).to(torch.bfloat16))
     ro, rl = oracle.attention_fwd(q, k, v, att.scale, True, 0, 0, window=window)
-    check_o(to_np(o), ro, "bf16")
+    check_o(to_np(o), ro, "bf16", stored_bf16=True)
     rq, rk, rv = oracle.attention_bwd(q, k, v, to_np(o), rl, do, att.scale, True, 0, 0,
                                       window=window)
     for g, r, name in ((tq.grad, rq, "dQ"), (tk.grad, rk, "dK"), (tv.grad, rv, "dV")):
