@@ -139,49 +139,45 @@ void dq_bf16_kernel(BwdArgs a) {
     const lds_u16* Ks = smem + (kt & 1) * C::STAGE;
     const lds_u16* Vs = Ks + C::TILE;
     const int64_t key0 = int64_t(kt) * BN;
-    if constexpr (FULL) {
-      if (wave_active) {
-        f32x16 s, dp;
-        sdp(Ks, Vs, 0, s, dp);
-#pragma unroll 1
-        for (int kb = 0; kb < C::NSB - 1; ++kb) {
-          f32x16 s2, dp2;
-          sdp(Ks, Vs, kb + 1, s2, dp2);  // independent of the vector work below
-          update(Ks, kb, s, dp);
-          s = s2;
-          dp = dp2;
-        }
-        update(Ks, C::NSB - 1, s, dp);
-      }
-    } else {
-      int nsb = 0, kb0 = 0;
-      if (wave_active) {
-        int64_t vis_last = a.len_kv - 1 - key0;
-        if (a.causal) vis_last = min(vis_last, a.q_start + (w_hi - 1) - a.kv_start - key0);
-        nsb = vis_last < 0 ? 0 : int(min<int64_t>(C::NSB, vis_last / 32 + 1));
-        const int64_t vis_first = a.q_start + w_lo - a.win + 1 - a.kv_start - key0;
-        if (vis_first > 0) kb0 = int(min<int64_t>(C::NSB, vis_first / 32));
-      }
-#pragma unroll 1
-      for (int kb = kb0; kb < nsb; ++kb) {
-        f32x16 s, dp;
-        sdp(Ks, Vs, kb, s, dp);
-        const int64_t kfirst = key0 + kb * 32;
-        if ((a.causal && a.kv_start + kfirst + 31 > a.q_start + w_lo) || kfirst + 32 > a.len_kv ||
-            a.q_start + (w_hi - 1) - (a.kv_start + kfirst) >= a.win) {
-          // hidden scores -> -inf, so P = exp2(-inf) = 0 (c > 0)
-          int64_t vlim64 = a.len_kv - 1 - kfirst;
-          if (a.causal) vlim64 = min(vlim64, a.q_start + row - a.kv_start - kfirst);
-          const int vlim = clamp_off(vlim64);
-          const int vmin = clamp_off(a.q_start + row - a.win + 1 - a.kv_start - kfirst);
+    // Every tile runs software-pipelined over its 32-key sub-blocks, mask-free
+    // when every row of this wave sees it whole (always, in a fully visible
+    // pair); otherwise each sub-block's hidden scores become -inf, so P =
+    // exp2(-inf) = 0 (c > 0).  Tiles no row of the wave sees are skipped.
+    bool run = wave_active, whole = FULL;
+    if constexpr (!FULL) {
+      whole = key0 + BN <= a.len_kv &&
+              (!a.causal || a.kv_start + key0 + BN - 1 <= a.q_start + w_lo) &&
+              a.q_start + (w_hi - 1) - (a.kv_start + key0) < a.win;
+      run = run && (!a.causal || a.kv_start + key0 <= a.q_start + w_hi - 1) &&
+            a.q_start + w_lo - (a.kv_start + min(key0 + BN, a.len_kv) - 1) < a.win;
+    }
+    auto mask = [&](f32x16& s, int kb) {
+      if (whole) return;
+      const int64_t kfirst = key0 + kb * 32;
+      int64_t vlim64 = a.len_kv - 1 - kfirst;
+      if (a.causal) vlim64 = min(vlim64, a.q_start + row - a.kv_start - kfirst);
+      const int vlim = clamp_off(vlim64);
+      const int vmin = clamp_off(a.q_start + row - a.win + 1 - a.kv_start - kfirst);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int off = 8 * (r >> 2) + 4 * hi + (r & 3);
-            if (off > vlim || off < vmin) s[r] = -INFINITY;
-          }
-        }
-        update(Ks, kb, s, dp);
+      for (int r = 0; r < 16; ++r) {
+        const int off = 8 * (r >> 2) + 4 * hi + (r & 3);
+        if (off > vlim || off < vmin) s[r] = -INFINITY;
       }
+    };
+    if (run) {
+      f32x16 s, dp;
+      sdp(Ks, Vs, 0, s, dp);
+#pragma unroll 1
+      for (int kb = 0; kb < C::NSB - 1; ++kb) {
+        f32x16 s2, dp2;
+        sdp(Ks, Vs, kb + 1, s2, dp2);  // independent of the vector work below
+        mask(s, kb);
+        update(Ks, kb, s, dp);
+        s = s2;
+        dp = dp2;
+      }
+      mask(s, C::NSB - 1);
+      update(Ks, C::NSB - 1, s, dp);
     }
     wait_vmem();  // the next tile's segments this wave staged have landed
     __syncthreads();

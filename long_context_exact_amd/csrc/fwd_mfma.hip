@@ -207,50 +207,46 @@ void fwd_bf16_kernel(FwdArgs a) {
                                          a.q_start + q_hi - 1 - (a.kv_start + key0) >= a.win);
       a.visits[int64_t(qt) * a.n_ktiles + kt] = straddle ? 2 : 1;
     }
-    if constexpr (FULL) {
-      if (wave_active) {
-        f32x16 s_cur = qk(Ks, 0);
-#pragma unroll  // unrolled: s_cur / s_nxt rename instead of being copied
-        for (int kb = 0; kb < C::NSB - 1; ++kb) {
-          f32x16 s_nxt = qk(Ks, kb + 1);  // independent of the softmax below
-          softmax(s_cur);
-          pv(Vs, kb, s_cur);
-          s_cur = s_nxt;
-        }
-        softmax(s_cur);
-        pv(Vs, C::NSB - 1, s_cur);
-      }
-    } else {
-      // Visible 32-key sub-blocks of this tile for this wave's rows: up to
-      // the causal limit of the last row, from the window start of the first.
-      int nsb = 0, kb0 = 0;
-      if (wave_active) {
-        int64_t vis_last = a.len_kv - 1 - key0;  // last key offset inside the chunk
-        if (a.causal) vis_last = min(vis_last, a.q_start + (w_hi - 1) - a.kv_start - key0);
-        nsb = vis_last < 0 ? 0 : int(min<int64_t>(C::NSB, vis_last / 32 + 1));
-        const int64_t vis_first = a.q_start + w_lo - a.win + 1 - a.kv_start - key0;
-        if (vis_first > 0) kb0 = int(min<int64_t>(C::NSB, vis_first / 32));
-      }
-#pragma unroll 1
-      for (int kb = kb0; kb < nsb; ++kb) {
-        f32x16 s = qk(Ks, kb);
-        const int64_t kfirst = key0 + kb * 32;
-        if ((a.causal && a.kv_start + kfirst + 31 > a.q_start + w_lo) || kfirst + 32 > a.len_kv ||
-            a.q_start + (w_hi - 1) - (a.kv_start + kfirst) >= a.win) {
-          // hidden scores become -inf; exp2 of them is exactly 0 (c > 0)
-          int64_t vlim64 = a.len_kv - 1 - kfirst;
-          if (a.causal) vlim64 = min(vlim64, a.q_start + row - a.kv_start - kfirst);
-          const int vlim = clamp_off(vlim64);
-          const int vmin = clamp_off(a.q_start + row - a.win + 1 - a.kv_start - kfirst);
+    // Every tile runs software-pipelined over its 32-key sub-blocks.  A tile
+    // that every row of this wave sees whole (always, in a fully visible
+    // pair) is mask-free; in any other tile each sub-block's hidden scores
+    // become -inf, so exp2 of them is exactly 0 (c > 0) and a sub-block no
+    // row sees adds nothing.  Tiles no row of the wave sees are skipped.
+    bool run = wave_active, whole = FULL;
+    if constexpr (!FULL) {
+      whole = key0 + BN <= a.len_kv &&
+              (!a.causal || a.kv_start + key0 + BN - 1 <= a.q_start + w_lo) &&
+              a.q_start + (w_hi - 1) - (a.kv_start + key0) < a.win;
+      // some key of the tile inside some row's window and causal limit
+      run = run && (!a.causal || a.kv_start + key0 <= a.q_start + w_hi - 1) &&
+            a.q_start + w_lo - (a.kv_start + min(key0 + BN, a.len_kv) - 1) < a.win;
+    }
+    auto mask = [&](f32x16& s, int kb) {
+      if (whole) return;
+      const int64_t kfirst = key0 + kb * 32;
+      int64_t vlim64 = a.len_kv - 1 - kfirst;
+      if (a.causal) vlim64 = min(vlim64, a.q_start + row - a.kv_start - kfirst);
+      const int vlim = clamp_off(vlim64);
+      const int vmin = clamp_off(a.q_start + row - a.win + 1 - a.kv_start - kfirst);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int off = 8 * (r >> 2) + 4 * hi + (r & 3);
-            if (off > vlim || off < vmin) s[r] = -INFINITY;
-          }
-        }
-        softmax(s);
-        pv(Vs, kb, s);
+      for (int r = 0; r < 16; ++r) {
+        const int off = 8 * (r >> 2) + 4 * hi + (r & 3);
+        if (off > vlim || off < vmin) s[r] = -INFINITY;
       }
+    };
+    if (run) {
+      f32x16 s_cur = qk(Ks, 0);
+#pragma unroll  // unrolled: s_cur / s_nxt rename instead of being copied
+      for (int kb = 0; kb < C::NSB - 1; ++kb) {
+        f32x16 s_nxt = qk(Ks, kb + 1);  // independent of the softmax below
+        mask(s_cur, kb);
+        softmax(s_cur);
+        pv(Vs, kb, s_cur);
+        s_cur = s_nxt;
+      }
+      mask(s_cur, C::NSB - 1);
+      softmax(s_cur);
+      pv(Vs, C::NSB - 1, s_cur);
     }
     wait_vmem();  // the next tile's segments this wave staged have landed
     __syncthreads();
