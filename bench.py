@@ -55,14 +55,16 @@ def source_digest(name: str) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_of(name: str, launches: int):
+def traffic_of(name: str, launches: int, workload: str):
     """HBM bytes per launch of `name` from the committed counter summary, or
-    None if there is none or the kernel's sources changed since it was taken."""
+    None if there is none, it was taken on another workload, or the kernel's
+    sources changed since it was taken."""
     try:
-        t = json.load(open(TRAFFIC_FILE))["kernels"][name]
+        doc = json.load(open(TRAFFIC_FILE))
+        t = doc["kernels"][name]
     except (OSError, KeyError, ValueError):
         return None
-    if t.get("source_digest") != source_digest(name):
+    if doc.get("workload") != workload or t.get("source_digest") != source_digest(name):
         return None
     return {"bytes_per_launch": t["bytes_per_launch"], "fetch": t["fetch_bytes_per_launch"],
             "write": t["write_bytes_per_launch"], "workload": t["workload"]}
@@ -72,16 +74,28 @@ def pairs_of(kind: int, c: int) -> int:
     return c * (c + 1) // 2 if kind == 0 else c * c
 
 
-def visible_pairs(item, c: int, window: int) -> int:
-    """(query, key) pairs of a chunk pair that the mask keeps: the causal
-    prefix, cut to the keys less than `window` positions behind the query."""
-    if window <= 0:
+def item_keys(item, c: int, n_global: int):
+    """(first key position, end position, window) of an item: the global
+    prefix (kv chunk -1, no window), chunk 0 past the global prefix, or the
+    whole kv chunk."""
+    kc = item[3]
+    if kc == -1:
+        return 0, n_global, 0
+    return (n_global if kc == 0 else kc * c), (kc + 1) * c, None
+
+
+def visible_pairs(item, c: int, window: int, n_global: int = 0) -> int:
+    """(query, key) pairs of an item that the mask keeps: the causal prefix
+    of its keys, cut to the keys less than `window` positions behind the
+    query (the global item's keys are never cut)."""
+    k0, k1, win = item_keys(item, c, n_global)
+    win = window if win is None else win
+    if win <= 0 and k0 == item[3] * c and k1 - k0 == c:
         return pairs_of(item[4], c)
     import numpy as np
     qpos = item[2] * c + np.arange(c, dtype=np.int64)
-    k0 = item[3] * c
-    hi = np.minimum(c - 1, qpos - k0)                # last visible key (local)
-    lo = np.maximum(0, qpos - window + 1 - k0)       # first visible key (local)
+    hi = np.minimum(k1 - 1, qpos)                                  # last visible key
+    lo = k0 if win <= 0 else np.maximum(k0, qpos - win + 1)        # first visible key
     return int(np.maximum(hi - lo + 1, 0).sum())
 
 
@@ -101,10 +115,11 @@ def gen_inputs(w, chunks_q, chunks_kv, backward):
     return out
 
 
-def cpu_baseline(w, host, worker, budget_s):
+def cpu_baseline(w, host, worker, budget_s, kv_lo):
     """The float64 oracle, as it stands, on a bounded sample of the same
     workload: the last R query rows of the measured query chunk, query head 0,
-    over their whole causal prefix, forward + backward."""
+    over their whole causal prefix, forward + backward.  kv_lo: the lowest
+    key chunk of the owner's chunk pairs (the global item aside)."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -112,10 +127,18 @@ def cpu_baseline(w, host, worker, budget_s):
 
     a = worker if worker >= 0 else w.workers - 1
     c = w.chunk
-    kvc = sorted(j for j in host[1] if j <= a)   # the key chunks the rows' keys live in
-    k0 = kvc[0] * c
-    kpre = np.concatenate([host[1][j][:, :, :1] for j in kvc], axis=1).astype(np.float64)
-    vpre = np.concatenate([host[2][j][:, :, :1] for j in kvc], axis=1).astype(np.float64)
+    # the rows' keys as contiguous position ranges (k0, k1, window): the
+    # window's chunks, and with global tokens also the global prefix
+    g = w.n_global
+    ranges = [((g if kv_lo == 0 else kv_lo * c), (a + 1) * c, w.window)]
+    if g > 0:
+        ranges.insert(0, (0, g, 0))
+
+    def keys(k0, k1, tid):
+        chunks = [host[tid][j][:, :, :1] for j in range(k0 // c, (k1 - 1) // c + 1)]
+        return np.concatenate(chunks, axis=1)[:, k0 % c:k0 % c + (k1 - k0)].astype(np.float64)
+
+    parts = [(keys(k0, k1, 1), keys(k0, k1, 2), k0, win) for k0, k1, win in ranges]
 
     def run(r):
         q = host[0][a][:, c - r:, :1].astype(np.float64)
@@ -123,13 +146,20 @@ def cpu_baseline(w, host, worker, budget_s):
             np.ones_like(q)
         q0 = a * c + c - r
         t0 = time.perf_counter()
-        o, lse = oracle.attention_fwd(q, kpre, vpre, w.scale, True, q0, k0, window=w.window)
+        outs = [oracle.attention_fwd(q, kp, vp, w.scale, True, q0, k0, window=win)
+                for kp, vp, k0, win in parts]
+        o, lse = outs[0] if len(outs) == 1 else oracle.lse_merge([x[0] for x in outs],
+                                                                  [x[1] for x in outs])
         t1 = time.perf_counter()
-        oracle.attention_bwd(q, kpre, vpre, o, lse, do, w.scale, True, q0, k0, window=w.window)
+        for kp, vp, k0, win in parts:
+            oracle.attention_bwd(q, kp, vp, o, lse, do, w.scale, True, q0, k0, window=win)
         t2 = time.perf_counter()
         pos = q0 + np.arange(r)
-        seen = pos - k0 + 1 if w.window <= 0 else np.minimum(w.window, pos - k0 + 1)
-        pairs = int(seen.sum())
+        pairs = 0
+        for kp, _, k0, win in parts:
+            hi = np.minimum(k0 + kp.shape[1] - 1, pos)
+            lo = k0 if win <= 0 else np.maximum(k0, pos - win + 1)
+            pairs += int(np.maximum(hi - lo + 1, 0).sum())
         return t2 - t0, pairs * 14 * w.head_dim, (t1 - t0, pairs * 4 * w.head_dim), \
             (t2 - t1, pairs * 10 * w.head_dim)
 
@@ -148,8 +178,10 @@ def cpu_baseline(w, host, worker, budget_s):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads or 1),
             "kind": "oracle",
             "sample": f"float64 numpy oracle ({lib}), fwd+bwd of the last {r} query rows of chunk "
-                      f"{a}, query head 0, over every key they see (keys {k0}..{a * c + c - 1}"
-                      f"{f', window {w.window}' if w.window else ''}); "
+                      f"{a}, query head 0, over every key they see (keys "
+                      f"{', '.join(f'{k0}..{k1 - 1}' for k0, k1, _ in ranges)}"
+                      f"{f', window {w.window}' if w.window else ''}"
+                      f"{f', the first {g} global' if g else ''}); "
                       f"{dt:.1f} s, {flops:.3e} algorithmic FLOP",
             "fwd_gflops": round(fw[1] / fw[0] / 1e9, 2), "bwd_gflops": round(bw[1] / bw[0] / 1e9, 2)}
 
@@ -196,7 +228,7 @@ def main():
     dev = "cuda"
     td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     att = ChunkedCausalAttention(w.workers, w.chunk, w.batch, w.heads_q, w.heads_kv, w.head_dim,
-                                 w.dtype, True, window=w.window)
+                                 w.dtype, True, window=w.window, n_global=w.n_global)
     if w.share_of >= 0:
         owners = [w.share_of]
         timed = att.items_of_worker(w.share_of)
@@ -206,7 +238,7 @@ def main():
         owners = list(range(w.workers))
         timed = att.items
         merged = {a: att.items_of_owner(a) for a in owners}
-    kv_needed = sorted({it[3] for its in merged.values() for it in its})
+    kv_needed = sorted({att.kv_rows(it[3])[0] for its in merged.values() for it in its})
 
     t0 = time.perf_counter()
     host = gen_inputs(w, owners, kv_needed, w.backward)
@@ -223,7 +255,7 @@ def main():
     lse = {a: torch.empty(att.lse_shape(), device=dev) for a in owners}
     delta = {a: torch.empty(att.lse_shape(), device=dev) for a in owners}
     dq = {a: torch.zeros(att.q_shape(), device=dev) for a in owners}
-    own_kv = sorted({it[3] for it in timed})
+    own_kv = sorted({att.kv_rows(it[3])[0] for it in timed})
     dk = {c: torch.zeros(att.kv_shape(), device=dev) for c in own_kv}
     dv = {c: torch.zeros(att.kv_shape(), device=dev) for c in own_kv}
 
@@ -241,7 +273,7 @@ def main():
             att.backward_items(timed, q, k, v, o, lse, d_o, delta, dq, dk, dv)
 
     per_pair = w.batch * w.heads_q * w.head_dim
-    n_pairs = sum(visible_pairs(it, w.chunk, w.window) for it in timed)
+    n_pairs = sum(visible_pairs(it, w.chunk, w.window, w.n_global) for it in timed)
     fwd_flop = n_pairs * per_pair * 4
     bwd_flop = n_pairs * per_pair * 10 if w.backward else 0
     flop = fwd_flop + bwd_flop
@@ -280,13 +312,20 @@ def main():
         return sum(a.elapsed_time(b) for a, b in evs)
 
     def fwd_call(it):
-        dfa.dfa_attn_fwd_partial(att.desc(it[2], it[3]), q[it[2]], k[it[3]], v[it[3]],
-                                 *partials[(it[2], it[3])])
+        a, kc = it[2], it[3]
+        o_part, l_part = partials[(a, kc)]
+        for d, bs, src, rs in att.calls(a, kc):
+            dfa.dfa_attn_fwd_partial(d, q[a][bs], k[src][bs, rs], v[src][bs, rs], o_part[bs],
+                                     l_part[bs])
 
     def bwd_call(part):
-        return lambda it: dfa.dfa_test_bwd_part(att.desc(it[2], it[3]), q[it[2]], k[it[3]],
-                                                v[it[3]], lse[it[2]], d_o[it[2]], delta[it[2]],
-                                                dq[it[2]], dk[it[3]], dv[it[3]], part)
+        def call(it):
+            a, kc = it[2], it[3]
+            for d, bs, src, rs in att.calls(a, kc):
+                dfa.dfa_test_bwd_part(d, q[a][bs], k[src][bs, rs], v[src][bs, rs], lse[a][bs],
+                                      d_o[a][bs], delta[a][bs], dq[a][bs], dk[src][bs, rs],
+                                      dv[src][bs, rs], part)
+        return call
 
     pairs_x_heads = n_pairs * w.batch * w.heads_q
     # name in the profiler, time per step, flop per step (the kernel's own
@@ -303,7 +342,7 @@ def main():
     achieved = kflop / (kms * 1e-3) / 1e12
     roofline = {"bound": "mfma" if w.dtype == "bf16" else "alu", "kernel": name, "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": traffic_of(name, nl), "avg_launch_ms": round(kms / nl, 3),
+                "traffic": traffic_of(name, nl, w.name), "avg_launch_ms": round(kms / nl, 3),
                 "launches_per_step": nl, "flop_per_launch": kflop / nl,
                 "others": {n: {"avg_launch_ms": round(x[0] / nl, 3),
                                "tflops": round(x[1] / (x[0] * 1e-3) / 1e12, 2)}
@@ -323,6 +362,7 @@ def main():
                    "share": (f"worker {w.share_of} of {w.workers}" if w.share_of >= 0
                              else "all pairs"),
                    "pairs_timed": len(timed), "backward": w.backward, "window": w.window,
+                   "n_global": w.n_global,
                    "algorithmic_flop_per_step": flop, "wall_s_timed": round(wall, 3),
                    "input_gen_s": round(gen_s, 1)},
         "roofline": roofline,
@@ -330,7 +370,9 @@ def main():
     if not args.no_cpu_baseline:
         del q, k, v, d_o, partials, o, lse, delta, dq, dk, dv
         torch.cuda.empty_cache()
-        result["cpu_baseline"] = cpu_baseline(w, host, w.share_of, args.cpu_seconds)
+        a = w.share_of if w.share_of >= 0 else w.workers - 1
+        kv_lo = min(it[3] for it in att.items_of_owner(a) if it[3] >= 0)
+        result["cpu_baseline"] = cpu_baseline(w, host, w.share_of, args.cpu_seconds, kv_lo)
     print(json.dumps(result), flush=True)
 
 

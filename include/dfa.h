@@ -56,8 +56,10 @@ typedef enum { DFA_F32 = 0, DFA_BF16 = 1 } dfa_dtype;
 /* One chunk pair of a schedule.  kind: 0 = diagonal pair (q_chunk ==
  * kv_chunk, needs the causal element mask), 1 = full pair (q_chunk >
  * kv_chunk, every score visible), 2 = band pair (q_chunk > kv_chunk, a
- * sliding window hides part of it).  owner = q_chunk: the worker whose
- * query rows these are; owner != worker marks a helper item. */
+ * sliding window hides part of it), 3 = global item (kv_chunk = -1: the
+ * query chunk against the replicated global tokens, see
+ * dfa_global_window_schedule).  owner = q_chunk: the worker whose query
+ * rows these are; owner != worker marks a helper item. */
 typedef struct {
   int32_t step, worker, q_chunk, kv_chunk, kind, owner;
 } dfa_work_item;
@@ -114,6 +116,25 @@ dfa_status dfa_window_schedule(int32_t num_workers, int64_t chunk_len,
                                int64_t window, dfa_work_item* items,
                                int64_t capacity, int64_t* num_items,
                                int32_t* num_steps);
+
+/* Sliding window plus global tokens replicated on every worker
+ * ([DistFlashAttn App. F]: for global attention the global tokens can be
+ * replicated on all workers, so that no step has to gather them).  The
+ * global tokens are the first n_global positions of the sequence
+ * (1 <= n_global <= chunk_len, all in chunk 0); a query sees its window
+ * (as in dfa_window_schedule) and every global token at or before it.
+ * Items: the window schedule's, except that a pair over kv chunk 0 covers
+ * only that chunk's keys n_global..chunk_len-1 (dropped when n_global =
+ * chunk_len), plus one global item per worker at step 0, listed before the
+ * worker's other step-0 item: (0, w, w, -1, 3, w), the worker's queries
+ * against the n_global global keys (global positions 0..n_global-1, causal,
+ * no window), read from the worker's replica.  Every visible (query, key)
+ * pair lies in exactly one item's key range.  Array, capacity and counts as
+ * in dfa_balanced_schedule. */
+dfa_status dfa_global_window_schedule(int32_t num_workers, int64_t chunk_len,
+                                      int64_t window, int64_t n_global,
+                                      dfa_work_item* items, int64_t capacity,
+                                      int64_t* num_items, int32_t* num_steps);
 
 /* Partial attention of one chunk pair: the normalised output and its LSE
  * ([DistFlashAttn App. D]: the forward returns output and logsumexp values;

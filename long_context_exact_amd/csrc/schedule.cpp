@@ -100,3 +100,46 @@ extern "C" dfa_status dfa_window_schedule(int32_t num_workers, int64_t chunk_len
   }
   return DFA_OK;
 }
+
+extern "C" dfa_status dfa_global_window_schedule(int32_t num_workers, int64_t chunk_len,
+                                                 int64_t window, int64_t n_global,
+                                                 dfa_work_item* items, int64_t capacity,
+                                                 int64_t* num_items, int32_t* num_steps) {
+  using dfa::fail;
+  const std::string fn = "dfa_global_window_schedule";
+  if (num_items == nullptr || num_steps == nullptr)
+    return fail(DFA_ERR_INVALID, fn + ": num_items and num_steps must be non-null");
+  if (num_workers < 1 || num_workers > 65536)
+    return fail(DFA_ERR_INVALID, fn + ": num_workers must be in [1, 65536], got " +
+                                     std::to_string(num_workers));
+  if (chunk_len < 1 || window < 1)
+    return fail(DFA_ERR_INVALID, fn + ": chunk_len and window must be >= 1");
+  if (n_global < 1 || n_global > chunk_len)
+    return fail(DFA_ERR_INVALID, fn + ": n_global must be in [1, chunk_len], got " +
+                                     std::to_string(n_global));
+  if (capacity < 0 || (items == nullptr && capacity > 0))
+    return fail(DFA_ERR_INVALID, fn + ": bad capacity / items");
+  const int64_t p = num_workers;
+  int64_t steps = 1;  // as in the window schedule
+  while (steps < p && (steps - 1) * chunk_len + 1 < window) ++steps;
+  // a pair over chunk 0 keeps keys n_global..C-1; none is left when n_global = C
+  const bool drop0 = n_global == chunk_len;
+  int64_t total = p;  // one global item per worker
+  for (int64_t t = 0; t < steps; ++t) total += (p - t) - (drop0 ? 1 : 0);
+  *num_items = total;
+  *num_steps = int32_t(steps);
+  if (capacity < total)
+    return fail(DFA_ERR_CAPACITY, fn + ": capacity " + std::to_string(capacity) +
+                                      " < required " + std::to_string(total));
+  int64_t n = 0;
+  for (int64_t t = 0; t < steps; ++t) {
+    const int32_t kind = t == 0 ? 0 : ((t + 1) * chunk_len - 1 < window ? 1 : 2);
+    for (int64_t w = t; w < p; ++w) {
+      if (t == 0)  // the worker's global item comes first (kv chunk -1)
+        items[n++] = {0, int32_t(w), int32_t(w), -1, 3, int32_t(w)};
+      if (drop0 && w - t == 0) continue;
+      items[n++] = {int32_t(t), int32_t(w), int32_t(w), int32_t(w - t), kind, int32_t(w)};
+    }
+  }
+  return DFA_OK;
+}

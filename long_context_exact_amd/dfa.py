@@ -21,13 +21,14 @@ from .build import LIB_PATH
 
 DFA_OK, DFA_ERR_INVALID, DFA_ERR_UNSUPPORTED, DFA_ERR_CAPACITY, DFA_ERR_HIP = range(5)
 DFA_F32, DFA_BF16 = 0, 1
-DIAG, FULL, BAND = 0, 1, 2
+DIAG, FULL, BAND, GLOBAL = 0, 1, 2, 3
 
 _DTYPES = {"f32": DFA_F32, "bf16": DFA_BF16}
 _TORCH = {DFA_F32: torch.float32, DFA_BF16: torch.bfloat16}
 
 EXPORTED = (
-    "dfa_balanced_schedule", "dfa_window_schedule", "dfa_attn_fwd_partial", "dfa_lse_merge", "dfa_attn_bwd",
+    "dfa_balanced_schedule", "dfa_window_schedule", "dfa_global_window_schedule",
+    "dfa_attn_fwd_partial", "dfa_lse_merge", "dfa_attn_bwd",
     "dfa_last_error", "dfa_version", "dfa_test_tile_shape", "dfa_test_fwd_tile_visits",
     "dfa_test_bwd_part",
 )
@@ -80,6 +81,8 @@ def lib() -> ctypes.CDLL:
                                             ctypes.POINTER(I64), ctypes.POINTER(I32)]
         L.dfa_window_schedule.argtypes = [I32, I64, I64, ctypes.POINTER(WorkItem), I64,
                                           ctypes.POINTER(I64), ctypes.POINTER(I32)]
+        L.dfa_global_window_schedule.argtypes = [I32, I64, I64, I64, ctypes.POINTER(WorkItem), I64,
+                                                 ctypes.POINTER(I64), ctypes.POINTER(I32)]
         L.dfa_attn_fwd_partial.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P]
         L.dfa_lse_merge.argtypes = [I32, ctypes.POINTER(P), ctypes.POINTER(P), I32, I32, I64, I32,
                                     I32, P, P, P]
@@ -89,7 +92,8 @@ def lib() -> ctypes.CDLL:
         L.dfa_test_fwd_tile_visits.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P]
         L.dfa_test_bwd_part.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, P, P, I32,
                                         P]
-        for name in ("dfa_balanced_schedule", "dfa_window_schedule", "dfa_attn_fwd_partial", "dfa_lse_merge",
+        for name in ("dfa_balanced_schedule", "dfa_window_schedule", "dfa_global_window_schedule",
+                     "dfa_attn_fwd_partial", "dfa_lse_merge",
                      "dfa_attn_bwd", "dfa_test_tile_shape", "dfa_test_fwd_tile_visits",
                      "dfa_test_bwd_part"):
             getattr(L, name).restype = I32
@@ -172,6 +176,21 @@ def dfa_window_schedule(num_workers: int, chunk_len: int, window: int):
     arr = (WorkItem * max(n.value, 1))()
     _check(lib().dfa_window_schedule(int(num_workers), int(chunk_len), int(window), arr, n.value,
                                      ctypes.byref(n), ctypes.byref(steps)))
+    return [arr[i].astuple() for i in range(n.value)], int(steps.value)
+
+
+def dfa_global_window_schedule(num_workers: int, chunk_len: int, window: int, n_global: int):
+    """(items as tuples, num_steps) of the sliding window plus replicated
+    global tokens (global items have kv_chunk -1 and kind GLOBAL)."""
+    n = ctypes.c_int64(0)
+    steps = ctypes.c_int32(0)
+    args = (int(num_workers), int(chunk_len), int(window), int(n_global))
+    st = lib().dfa_global_window_schedule(*args, None, 0, ctypes.byref(n), ctypes.byref(steps))
+    if st not in (DFA_OK, DFA_ERR_CAPACITY):
+        _check(st)
+    arr = (WorkItem * max(n.value, 1))()
+    _check(lib().dfa_global_window_schedule(*args, arr, n.value, ctypes.byref(n),
+                                            ctypes.byref(steps)))
     return [arr[i].astuple() for i in range(n.value)], int(steps.value)
 
 

@@ -1,12 +1,22 @@
 """Host orchestration of the chunked causal attention on one GPU.
 
 P virtual workers hold P contiguous chunks of C tokens ([DistFlashAttn
-§3.1]).  The schedule (from libdfa's dfa_balanced_schedule, or
-dfa_window_schedule for a local sliding window, App. F) lists the
-(query chunk, key/value chunk) pairs; each pair is one dfa_attn_fwd_partial
-call, an owner's partials are combined by dfa_lse_merge in ascending
-key/value chunk order, and the backward replays the owner's pairs through
-dfa_attn_bwd from the merged O and LSE.  On one GPU the workers are plain
+§3.1]).  The schedule (from libdfa's dfa_balanced_schedule, dfa_window_schedule
+for a local sliding window, or dfa_global_window_schedule for a window plus
+replicated global tokens, App. F) lists the (query chunk, key/value chunk)
+pairs; each pair is one dfa_attn_fwd_partial call, an owner's partials are
+combined by dfa_lse_merge in ascending key/value chunk order, and the
+backward replays the owner's pairs through dfa_attn_bwd from the merged O
+and LSE.
+
+With G global tokens (the first G positions, in chunk 0) a global item
+(kv chunk -1) reads keys 0..G-1 and a pair over chunk 0 reads keys G..C-1.
+Those key ranges are row ranges of chunk 0's tensors; the kernels take
+[B, len, H, d] contiguous tensors, so with B > 1 such a pair runs as one
+call per batch row (each a contiguous slice).  Every worker reads the same
+global rows: on one GPU the replicas the pages describe are one tensor,
+and their gradients (summed over workers by an all-reduce on many GPUs)
+add into the same dK/dV rows.  On one GPU the workers are plain
 work items on one stream; a helper's returned (O, LSE) is simply a buffer
 the owner's merge reads.
 
@@ -37,9 +47,15 @@ class ChunkedCausalAttention:
     balanced: bool = True
     scale: float | None = None
     window: int = 0  # 0: full causal attention; > 0: local sliding window of that many tokens
+    n_global: int = 0  # > 0 (with a window): the first n_global tokens are global
 
     def __post_init__(self):
-        if self.window > 0:
+        if self.n_global > 0:
+            if self.window <= 0:
+                raise ValueError("global tokens need a sliding window (else every key is visible)")
+            self.items, self.num_steps = dfa.dfa_global_window_schedule(
+                self.workers, self.chunk, self.window, self.n_global)
+        elif self.window > 0:
             self.items, self.num_steps = dfa.dfa_window_schedule(self.workers, self.chunk,
                                                                  self.window)
         else:
@@ -56,9 +72,34 @@ class ChunkedCausalAttention:
         return sorted((it for it in self.items if it[5] == a), key=lambda it: it[3])
 
     def desc(self, q_chunk: int, kv_chunk: int) -> dfa.AttnDesc:
+        """Descriptor of a pair over whole chunks (no global tokens involved)."""
         c = self.chunk
         return dfa.make_desc(self.batch, self.heads_q, self.heads_kv, self.head_dim, c, c,
                              q_chunk * c, kv_chunk * c, True, self.scale, self.dtype, self.window)
+
+    def kv_rows(self, kv_chunk: int):
+        """(source chunk, first row, end row, kv_start, window) of an item's keys."""
+        c, g = self.chunk, self.n_global
+        if kv_chunk == -1:            # global item: keys 0..G-1, causal, no window
+            return 0, 0, g, 0, 0
+        if kv_chunk == 0 and g > 0:   # chunk 0 past its global prefix
+            return 0, g, c, g, self.window
+        return kv_chunk, 0, c, kv_chunk * c, self.window
+
+    def calls(self, q_chunk: int, kv_chunk: int):
+        """The library calls of one item: (desc, batch slice, source chunk,
+        row slice); one call over every batch row unless the keys are a
+        sub-range of the chunk and B > 1."""
+        src, r0, r1, k0, win = self.kv_rows(kv_chunk)
+        c = self.chunk
+        if (r0 == 0 and r1 == c) or self.batch == 1:
+            parts = [(slice(None), self.batch)]
+        else:
+            parts = [(slice(b, b + 1), 1) for b in range(self.batch)]
+        for bs, nb in parts:
+            d = dfa.make_desc(nb, self.heads_q, self.heads_kv, self.head_dim, c, r1 - r0,
+                              q_chunk * c, k0, True, self.scale, self.dtype, win)
+            yield d, bs, src, slice(r0, r1)
 
     # ---- buffers --------------------------------------------------------
     def q_shape(self):
@@ -80,7 +121,9 @@ class ChunkedCausalAttention:
         for it in items:
             a, c = it[2], it[3]
             o_part, lse = partials[(a, c)]
-            dfa.dfa_attn_fwd_partial(self.desc(a, c), q[a], k[c], v[c], o_part, lse, stream)
+            for d, bs, src, rs in self.calls(a, c):
+                dfa.dfa_attn_fwd_partial(d, q[a][bs], k[src][bs, rs], v[src][bs, rs], o_part[bs],
+                                         lse[bs], stream)
 
     def merge_owner(self, a, partials, o_out, lse_out, stream=None):
         its = self.items_of_owner(a)
@@ -95,14 +138,19 @@ class ChunkedCausalAttention:
 
         o, lse, d_o, delta: query chunk -> tensors (final O and LSE).  The
         delta of a query chunk is computed on its first pair here and reused
-        (have_delta tracks which chunks already hold it)."""
+        (have_delta tracks which (chunk, batch row) pairs already hold it)."""
         have = set() if have_delta is None else have_delta
         for it in items:
             a, c = it[2], it[3]
-            first = a not in have
-            dfa.dfa_attn_bwd(self.desc(a, c), q[a], k[c], v[c], o[a] if first else None, lse[a],
-                             d_o[a], delta[a], first, dq[a], dk[c], dv[c], stream)
-            have.add(a)
+            for d, bs, src, rs in self.calls(a, c):
+                rows = range(self.batch) if bs.start is None else [bs.start]
+                first = (a, rows[0]) not in have
+                assert all(((a, b) not in have) == first for b in rows)
+                dfa.dfa_attn_bwd(d, q[a][bs], k[src][bs, rs], v[src][bs, rs],
+                                 o[a][bs] if first else None, lse[a][bs], d_o[a][bs],
+                                 delta[a][bs], first, dq[a][bs], dk[src][bs, rs],
+                                 dv[src][bs, rs], stream)
+                have.update((a, b) for b in rows)
         return have
 
     # ---- communication / computation overlap (one GPU, two streams) -------
@@ -123,6 +171,8 @@ class ChunkedCausalAttention:
         the computation (the non-overlapped baseline).  Results are bitwise
         those of `forward_items`."""
         items = sorted(self.items_of_worker(w), key=lambda it: it[0])
+        if self.n_global > 0:
+            raise ValueError("the overlap emulation exchanges whole chunks; global items have none")
         dev = q[w].device
         compute = torch.cuda.current_stream(dev)
         comm = torch.cuda.Stream(dev) if overlap else compute

@@ -67,6 +67,7 @@ class Workload:
     share_of: int       # -1: every chunk pair; w: worker w's share only
     batch: int = 1
     window: int = 0     # 0: full causal attention; > 0: local sliding window (tokens)
+    n_global: int = 0   # > 0 (with a window): the first n_global tokens are global
 
     @property
     def total_len(self) -> int:
@@ -99,4 +100,7 @@ WORKLOADS = {
     # the same worker share under a local sliding window of 4096 tokens
     "gqa64x8_512k_win4k_w15": Workload("gqa64x8_512k_win4k_w15", 32768, 16, 64, 8, 128, "bf16",
                                        1006, True, 15, window=4096),
+    # and with the first 1024 tokens global (replicated on every worker)
+    "gqa64x8_512k_win4k_g1k_w15": Workload("gqa64x8_512k_win4k_g1k_w15", 32768, 16, 64, 8, 128,
+                                           "bf16", 1007, True, 15, window=4096, n_global=1024),
 }

@@ -14,9 +14,11 @@ paper's section / figure / appendix as that page tags them.
 Modules
 -------
 attention  exact causal softmax attention (forward, LSE merge, backward),
-           optionally restricted to a local sliding window
-schedule   the chunk-pair schedules (unbalanced, load-balanced and
-           sliding-window) and the causal tile map of one chunk pair
+           optionally restricted to a local sliding window, with or without
+           global tokens
+schedule   the chunk-pair schedules (unbalanced, load-balanced, sliding-window
+           and sliding-window with replicated global tokens) and the causal
+           tile map of one chunk pair
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against facts the
 oracle does not compute itself (brute force, closed forms, invariants,
@@ -34,5 +36,6 @@ from .schedule import (  # noqa: F401
     balanced_schedule,
     unbalanced_schedule,
     window_schedule,
+    global_window_schedule,
     causal_tile_map,
 )

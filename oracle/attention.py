@@ -14,7 +14,9 @@ Notation (one head h of one batch row b):
     q0, k0     global token index of row 0 of the query / key chunk
     J(i)       visible keys of query i: {j : k0 + j <= q0 + i} when causal;
                with a sliding window of W tokens also q0 + i - (k0 + j) < W
-               (a query sees itself and the W - 1 tokens before it)
+               (a query sees itself and the W - 1 tokens before it); with
+               n_global = G > 0 global tokens, keys at positions < G are
+               visible through the window as well (each still counted once)
     s_ij       sigma * <Q_i, K_j>
     LSE_i      natural-log log-sum-exp of s_ij over J(i)   (-inf if J(i) empty)
     P_ij       exp(s_ij - LSE_i) on J(i), 0 elsewhere
@@ -50,31 +52,36 @@ def _check_shapes(q, k, v):
     return b, lq, hq, k.shape[1], hkv, d
 
 
-def _check_window(causal: bool, window: int) -> int:
-    window = int(window)
-    if window < 0:
-        raise ValueError("window must be >= 0")
-    if window > 0 and not causal:
-        raise ValueError("a sliding window applies to causal attention only")
-    return window
+def _check_window(causal: bool, window: int, n_global: int = 0):
+    window, n_global = int(window), int(n_global)
+    if window < 0 or n_global < 0:
+        raise ValueError("window and n_global must be >= 0")
+    if (window > 0 or n_global > 0) and not causal:
+        raise ValueError("a sliding window or global tokens apply to causal attention only")
+    return window, n_global
 
 
-def _visible(rows: np.ndarray, lk: int, q0: int, k0: int, causal: bool, window: int = 0):
+def _visible(rows: np.ndarray, lk: int, q0: int, k0: int, causal: bool, window: int = 0,
+             n_global: int = 0):
     """Boolean [len(rows), lk]: key j visible to query i (global positions,
     inclusive diagonal: a query sees itself and every earlier token, §3.2
     "each worker processes only its causal prefix").  window > 0 keeps only
     the keys less than `window` positions behind the query: the local
-    sliding window of [App. F], which lets a worker skip non-local keys."""
+    sliding window of [App. F], which lets a worker skip non-local keys.
+    n_global = G > 0 adds back the global tokens of App. F's global
+    attention, read as the first G positions of the sequence: a query also
+    sees every global token at or before it."""
     if not causal:
         return np.ones((rows.size, lk), dtype=bool)
-    dist = (q0 + rows[:, None]) - (k0 + np.arange(lk)[None, :])
+    kpos = k0 + np.arange(lk)[None, :]
+    dist = (q0 + rows[:, None]) - kpos
     vis = dist >= 0
     if window > 0:
-        vis &= dist < window
+        vis &= (dist < window) | (kpos < n_global)
     return vis
 
 
-def attention_fwd(q, k, v, scale, causal=True, q_start=0, kv_start=0, window=0):
+def attention_fwd(q, k, v, scale, causal=True, q_start=0, kv_start=0, window=0, n_global=0):
     """Exact attention output and LSE for one (query chunk, key/value chunk)
     block, or for a whole sequence (q_start = kv_start = 0).
 
@@ -85,9 +92,10 @@ def attention_fwd(q, k, v, scale, causal=True, q_start=0, kv_start=0, window=0):
 
     Returns (o [B,Lq,Hq,d] float64, lse [B,Hq,Lq] float64).  Rows that see
     no key get o = 0 and lse = -inf.  window > 0 (causal only): the local
-    sliding window described in [App. F].
+    sliding window described in [App. F]; n_global > 0 (with a window): the
+    first n_global positions are global tokens every later query sees.
     """
-    window = _check_window(causal, window)
+    window, n_global = _check_window(causal, window, n_global)
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -105,7 +113,7 @@ def attention_fwd(q, k, v, scale, causal=True, q_start=0, kv_start=0, window=0):
             for r0 in range(0, lq, rb):
                 rows = np.arange(r0, min(lq, r0 + rb))
                 s = scale * (q[bi, rows, h, :] @ kg.T)          # [R, Lk]
-                vis = _visible(rows, lk, q_start, kv_start, causal, window)
+                vis = _visible(rows, lk, q_start, kv_start, causal, window, n_global)
                 s = np.where(vis, s, -np.inf)
                 m = s.max(axis=1)                                # -inf if empty
                 live = np.isfinite(m)
@@ -158,7 +166,7 @@ def attention_delta(o, do):
 
 
 def attention_bwd(q, k, v, o, lse, do, scale, causal=True, q_start=0,
-                  kv_start=0, delta=None, window=0):
+                  kv_start=0, delta=None, window=0, n_global=0):
     """Gradients of L = sum_{i,h} <dO_i, O_i> restricted to one block of
     (query rows, key columns), from the *saved* final O and LSE.
 
@@ -174,11 +182,11 @@ def attention_bwd(q, k, v, o, lse, do, scale, causal=True, q_start=0,
     block of a sequence gives the whole-sequence gradient.
 
     o, do: [B,Lq,Hq,d]; lse: [B,Hq,Lq] (final, merged); delta: optional
-    [B,Hq,Lq] (computed from o and do when None); window as in
-    ``attention_fwd``.
+    [B,Hq,Lq] (computed from o and do when None); window and n_global as
+    in ``attention_fwd``.
     Returns (dq [B,Lq,Hq,d], dk [B,Lk,Hkv,d], dv [B,Lk,Hkv,d]) in float64.
     """
-    window = _check_window(causal, window)
+    window, n_global = _check_window(causal, window, n_global)
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -208,7 +216,7 @@ def attention_bwd(q, k, v, o, lse, do, scale, causal=True, q_start=0,
                 rows, row_lse = rows[live], row_lse[live]
                 qi, doi = q[bi, rows, h, :], do[bi, rows, h, :]
                 s = scale * (qi @ kg.T)
-                vis = _visible(rows, lk, q_start, kv_start, causal, window)
+                vis = _visible(rows, lk, q_start, kv_start, causal, window, n_global)
                 p = np.where(vis, np.exp(np.where(vis, s, 0.0) - row_lse[:, None]), 0.0)
                 dp = doi @ vg.T
                 ds = p * (dp - delta[bi, h, rows][:, None])

@@ -41,11 +41,12 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["balanced_schedule", "unbalanced_schedule", "window_schedule",
-           "causal_tile_map", "DIAG", "FULL", "BAND"]
+           "global_window_schedule", "causal_tile_map", "DIAG", "FULL", "BAND", "GLOBAL"]
 
 DIAG = 0
 FULL = 1
 BAND = 2
+GLOBAL = 3
 
 
 def unbalanced_schedule(num_workers: int):
@@ -97,6 +98,26 @@ def window_schedule(num_workers: int, chunk_len: int, window: int):
             items.append((t, w, w, w - t, kind, w))
         t += 1
     return items, t
+
+
+def global_window_schedule(num_workers: int, chunk_len: int, window: int, n_global: int):
+    """(items, num_steps) of a sliding window plus G = n_global global tokens
+    replicated on every worker ([App. F]: global tokens may be replicated so
+    that no step gathers them).  The global tokens are the first G positions
+    (G <= C, all in chunk 0).  Every worker w first does its global item
+    (step 0, kv chunk -1, kind GLOBAL): its queries against the G global
+    keys, from its own replica.  Its window items are those of
+    ``window_schedule``, except that a pair over chunk 0 covers only keys
+    G..C-1 (keys below G belong to the global item, so none is counted
+    twice) and is dropped when G = C.  Sorted by (step, worker, kv chunk)."""
+    p, c, w_, g = int(num_workers), int(chunk_len), int(window), int(n_global)
+    if g < 1 or g > c:
+        raise ValueError("n_global must be in [1, chunk_len]")
+    items, steps = window_schedule(p, c, w_)
+    items = [it for it in items if not (it[3] == 0 and g == c)]
+    items += [(0, w, w, -1, GLOBAL, w) for w in range(p)]
+    items.sort(key=lambda it: (it[0], it[1], it[3]))
+    return items, steps
 
 
 def causal_tile_map(len_q: int, len_k: int, q_start: int, kv_start: int,

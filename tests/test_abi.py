@@ -87,6 +87,34 @@ def test_window_schedule_argument_errors(dfa_lib):
     assert n.value == 15 and s.value == 2
 
 
+@pytest.mark.parametrize("p", [1, 2, 5, 16])
+@pytest.mark.parametrize("c", [1, 7, 128, 32768])
+@pytest.mark.parametrize("win_of_c", [0.001, 0.5, 1.0, 2.5])
+@pytest.mark.parametrize("g_of_c", [0.0, 0.03, 0.5, 1.0])
+def test_global_window_schedule_bit_exact_vs_oracle(dfa_lib, p, c, win_of_c, g_of_c):
+    win = max(1, int(win_of_c * c))
+    g = min(c, max(1, int(g_of_c * c)))
+    items, steps = dfa_lib.dfa_global_window_schedule(p, c, win, g)
+    ref, ref_steps = oracle.global_window_schedule(p, c, win, g)
+    assert steps == ref_steps
+    assert items == [tuple(x) for x in ref]
+
+
+def test_global_window_schedule_argument_errors(dfa_lib):
+    L = dfa_lib.lib()
+    n, s = ctypes.c_int64(-1), ctypes.c_int32(-1)
+    for args in ((0, 4, 4, 1), (4, 0, 4, 1), (4, 4, 0, 1), (4, 4, 4, 0), (4, 4, 4, 5),
+                 (70000, 4, 4, 1)):
+        assert L.dfa_global_window_schedule(*args, None, 0, ctypes.byref(n), ctypes.byref(s)) == \
+            D.DFA_ERR_INVALID
+        assert dfa_lib.dfa_last_error().startswith("dfa_global_window_schedule")
+    arr = (D.WorkItem * 3)()
+    # 8 global items + the window schedule's 15
+    assert L.dfa_global_window_schedule(8, 4, 4, 2, arr, 3, ctypes.byref(n), ctypes.byref(s)) == \
+        D.DFA_ERR_CAPACITY
+    assert n.value == 23 and s.value == 2
+
+
 def _fwd(L, d, q=FAKE, o=FAKE, lse=FAKE):
     return L.dfa_attn_fwd_partial(ctypes.byref(d) if d is not None else None, q, FAKE, FAKE, o,
                                   lse, None)

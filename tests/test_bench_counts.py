@@ -35,3 +35,17 @@ def test_visible_pairs_match_enumeration(p, chunk, window):
 def test_causal_pair_counts():
     assert bench.pairs_of(0, 32768) == 32768 * 32769 // 2
     assert bench.pairs_of(1, 32768) == 32768 ** 2
+
+
+@pytest.mark.parametrize("p,chunk,window,g", [(4, 8, 3, 2), (5, 6, 7, 6), (3, 7, 1, 1), (6, 5, 12, 3)])
+def test_global_visible_pairs_sum_to_the_masked_pairs(p, chunk, window, g):
+    """Summed over the global-window schedule, the counted pairs are exactly
+    the (query, key) pairs the global-token mask keeps."""
+    items = oracle.global_window_schedule(p, chunk, window, g)[0]
+    got = sum(bench.visible_pairs(it, chunk, window, g) for it in items)
+    want = sum(1 for i in range(p * chunk) for j in range(i + 1) if i - j < window or j < g)
+    assert got == want
+    for it in items:
+        if it[3] == -1:  # the global item: every causal key of the prefix
+            assert bench.visible_pairs(it, chunk, window, g) == sum(
+                min(g, it[2] * chunk + i + 1) for i in range(chunk))
