@@ -180,7 +180,14 @@ dfa_status dfa_lse_merge(int32_t n, const float* const* o_parts,
  * is 1 and read otherwise (pass 1 on the first pair of a query chunk and 0
  * on its other pairs).  dq, dk, dv accumulate (+=): the caller zeroes them
  * once and sums over pairs (App. D: the backward returns gradient partials
- * to their owners).  Each call is deterministic. */
+ * to their owners).  Each call is deterministic.  When few key blocks carry
+ * most of the pair's rows (a short key range against a long query chunk, a
+ * window band) the dK/dV part splits each block's rows over several
+ * workgroups and sums their partials in a fixed order, in a scratch buffer
+ * the library allocates once per device (grown on demand, kept until the
+ * process ends; growing it synchronizes the device).  Calls that split share
+ * that buffer: on one device they must not run concurrently (issue them on
+ * one stream); calls on one stream are ordered. */
 dfa_status dfa_attn_bwd(const dfa_attn_desc* desc, const void* q,
                         const void* k, const void* v, const void* o,
                         const float* lse, const void* d_o, float* delta,

@@ -24,7 +24,33 @@ struct BwdArgs {
   float c;      // scale * log2(e), > 0
   float scale;
   int64_t win;  // sliding window in tokens; a huge value when there is none
+  // dK/dV row split: each key block's steps are cut into rsplit slices run
+  // by separate workgroups (blockIdx.z), which store their partial dK, dV to
+  // ws ([2][rsplit][B][len_kv][Hkv][d] float32) for a fixed-order reduction;
+  // rsplit = 1 adds straight into dk, dv.
+  int32_t rsplit;
+  float* ws;
 };
+
+// The query-row steps of the dK/dV workgroup owning keys [k_lo, k_lo + bk):
+// rows from the first one at or after its first key to the last one whose
+// window still reaches its last key, in blocks of bq rows, times the
+// group's query heads.  Shared by the launcher, the kernel and the split
+// reduction, so all three agree on which slices exist.
+struct DkvSpan {
+  int qt0, nq, steps;
+};
+__host__ __device__ inline DkvSpan dkdv_span(const BwdArgs& a, int64_t k_lo, int bk, int bq) {
+  int64_t i_begin = 0;
+  if (a.causal) i_begin = a.kv_start + k_lo - a.q_start > 0 ? a.kv_start + k_lo - a.q_start : 0;
+  const int64_t k_last = (k_lo + bk < a.len_kv ? k_lo + bk : a.len_kv) - 1;
+  int64_t i_end = a.kv_start + k_last + a.win - a.q_start;
+  if (i_end > a.len_q) i_end = a.len_q;
+  if (i_begin >= i_end) return {0, 0, 0};
+  const int qt0 = int(i_begin / bq);
+  const int nq = int((i_end + bq - 1) / bq) - qt0;
+  return {qt0, nq, a.group * nq};
+}
 
 // LSE in base 2 for the exp2 form; a row without keys (LSE = -inf) gets +inf
 // so that its P is exactly 0.

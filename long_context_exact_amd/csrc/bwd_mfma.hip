@@ -61,6 +61,8 @@ dfa_status launch_bwd(const dfa_attn_desc& d, const void* q, const void* k, cons
   a.c = std::max(d.scale * kLog2e, FLT_MIN);
   a.scale = d.scale;
   a.win = d.window > 0 ? d.window : kNoWindow;
+  a.rsplit = 1;  // the dK/dV launcher may split rows
+  a.ws = nullptr;
   if (parts & 1) {
     const dfa_status st = launch_dkdv_bf16(d, a, s);
     if (st != DFA_OK) return st;

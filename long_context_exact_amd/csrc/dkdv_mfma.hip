@@ -2,6 +2,7 @@
 // backward; see bwd_mfma.hip for the pair of kernels and their contract).
 #include <algorithm>
 #include <cfloat>
+#include <mutex>
 
 #include "bwd_common.hpp"
 
@@ -56,17 +57,14 @@ void dkdv_bf16_kernel(BwdArgs a) {
   const int64_t q_rs = int64_t(a.hq) * D;
   const int64_t kv_rs = int64_t(a.hkv) * D;
 
-  // Query rows that see at least one key of this workgroup: from the first
-  // row at or after its first key, to the last row whose window still
-  // reaches its last key.
-  int64_t i_begin = 0;
-  if (a.causal) i_begin = max<int64_t>(0, a.kv_start + k_lo - a.q_start);
-  const int64_t i_end =
-      min<int64_t>(a.len_q, a.kv_start + min<int64_t>(k_lo + C::BK, a.len_kv) - 1 + a.win - a.q_start);
-  if (i_begin >= i_end) return;  // uniform over the workgroup
-  const int qt0 = int(i_begin / C::BQ);
-  const int nq = int(cdiv(i_end, C::BQ)) - qt0;
-  const int steps = a.group * nq;
+  // This workgroup's steps: its key block's query-row steps, or with a row
+  // split the blockIdx.z-th slice of them (uniform over the workgroup).
+  const DkvSpan sp = dkdv_span(a, k_lo, C::BK, C::BQ);
+  const int qt0 = sp.qt0, nq = sp.nq;
+  const int per = int(cdiv(sp.steps, a.rsplit));
+  const int it0 = int(blockIdx.z) * per;
+  const int it1 = min(sp.steps, it0 + per);
+  if (it0 >= it1) return;  // the reduction skips slices without steps
 
   // K of this lane's key as the B operand of S (elements d = 16*st + 8*hi
   // + e), in VGPRs for the whole loop; V rows of the workgroup in LDS.
@@ -148,19 +146,20 @@ void dkdv_bf16_kernel(BwdArgs a) {
     }
   };
 
-  stage_q(0, 0);
-  if (wave == 0) load_stats(0);
+  stage_q(it0, 0);
+  if (wave == 0) load_stats(it0);
   wait_vmem();
   if (wave == 0) store_stats(0);
   __syncthreads();
 
 #pragma unroll 1
-  for (int it = 0; it < steps; ++it) {
-    if (it + 1 < steps) {  // lands while this step computes
-      stage_q(it + 1, (it + 1) & 1);
+  for (int it = it0; it < it1; ++it) {
+    const int stage = (it - it0) & 1;
+    if (it + 1 < it1) {  // lands while this step computes
+      stage_q(it + 1, stage ^ 1);
       if (wave == 0) load_stats(it + 1);
     }
-    const lds_u16* Qs = stage_ptr(it & 1);
+    const lds_u16* Qs = stage_ptr(stage);
     const lds_u16* dOs = Qs + C::Q_TILE;
     const lds_f32* stats = reinterpret_cast<const lds_f32*>(Qs + 2 * C::Q_TILE);
     const int64_t r0 = int64_t(qt0 + it % nq) * C::BQ;  // first row of this step
@@ -241,14 +240,35 @@ void dkdv_bf16_kernel(BwdArgs a) {
     }
     // The next stage this wave staged (and, for wave 0, the next step's row
     // statistics) must land before the barrier.
-    if (it + 1 < steps) {
+    if (it + 1 < it1) {
       wait_vmem();
-      if (wave == 0) store_stats((it + 1) & 1);
+      if (wave == 0) store_stats(stage ^ 1);
     }
     __syncthreads();
   }
 
   if (!wave_active || key >= a.len_kv) return;
+  if (a.rsplit > 1) {  // store this slice's partial for the reduction
+    const int64_t n = int64_t(a.rsplit) * gridDim.y * a.len_kv * kv_rs;
+    float* wk = a.ws + ((int64_t(blockIdx.z) * gridDim.y + b) * a.len_kv + key) * kv_rs +
+                int64_t(g) * D;
+    float* wv = wk + n;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d = 32 * db + 8 * r4 + 4 * hi;
+        f32x4 xk, xv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xk[e] = a.scale * dk_acc[db][4 * r4 + e];
+          xv[e] = dv_acc[db][4 * r4 + e];
+        }
+        *reinterpret_cast<f32x4*>(wk + d) = xk;
+        *reinterpret_cast<f32x4*>(wv + d) = xv;
+      }
+    return;
+  }
   float* dkr = a.dk + (b * a.len_kv + key) * kv_rs + int64_t(g) * D;
   float* dvr = a.dv + (b * a.len_kv + key) * kv_rs + int64_t(g) * D;
 #pragma unroll
@@ -268,21 +288,112 @@ void dkdv_bf16_kernel(BwdArgs a) {
     }
 }
 
+// dk, dv += the row-split slices' partials, summed in slice order (so the
+// result does not depend on which slice finished first).  One thread per 4
+// consecutive elements of [B][len_kv][Hkv][d]; slices a key block did not
+// run (fewer steps than slices) are skipped exactly as the kernel skipped them.
+template <int BK, int BQ>
+__global__ __launch_bounds__(256) void dkdv_split_reduce_kernel(BwdArgs a, int64_t n4, int32_t row4) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const int64_t key = (i / row4) % a.len_kv;
+  const DkvSpan sp = dkdv_span(a, (key / BK) * BK, BK, BQ);
+  if (sp.steps == 0) return;
+  const int per = int(cdiv(sp.steps, a.rsplit));
+  const int used = int(cdiv(sp.steps, per));
+  const f32x4* wk = reinterpret_cast<const f32x4*>(a.ws);
+  const f32x4* wv = wk + int64_t(a.rsplit) * n4;
+  f32x4 sk = wk[i], sv = wv[i];
+  for (int z = 1; z < used; ++z) {
+    sk += wk[int64_t(z) * n4 + i];
+    sv += wv[int64_t(z) * n4 + i];
+  }
+  f32x4* dk = reinterpret_cast<f32x4*>(a.dk);
+  f32x4* dv = reinterpret_cast<f32x4*>(a.dv);
+  dk[i] += sk;
+  dv[i] += sv;
+}
+
+// Library-owned scratch for the split partials, one buffer per device, grown
+// on demand (kept until the process ends).
+float* split_workspace(size_t bytes) {
+  static std::mutex mu;
+  static void* ptr[64] = {};
+  static size_t cap[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cap[dev] >= bytes) return static_cast<float*>(ptr[dev]);
+  if (ptr[dev] != nullptr) {  // work queued with the old buffer must finish first
+    if (hipDeviceSynchronize() != hipSuccess || hipFree(ptr[dev]) != hipSuccess) return nullptr;
+    ptr[dev] = nullptr;
+    cap[dev] = 0;
+  }
+  void* p = nullptr;
+  if (hipMalloc(&p, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  ptr[dev] = p;
+  cap[dev] = bytes;
+  return static_cast<float*>(p);
+}
+
 constexpr int kDkvNW = 8;
+constexpr int kMaxSplit = 64;                                // slices per key block
+constexpr int kMinSplitSteps = 32;                           // steps per slice, at least
+constexpr size_t kMaxSplitBytes = size_t(4) << 30;           // workspace cap
 
 template <int D>
 dfa_status launch_dkdv(const dfa_attn_desc& d, BwdArgs a, hipStream_t s) {
   using C = DkvCfg<D, kDkvNW>;
-  dim3 grid(unsigned(cdiv(d.len_kv, C::BK)) * unsigned(d.heads_kv), unsigned(d.batch));
+  // Row split: when the longest key block's steps exceed twice an even
+  // share of all steps over the CUs (few key blocks with many rows: a short
+  // key range such as global tokens, or the blocks a window band reaches),
+  // cut every block's steps into slices that run as separate workgroups.
+  const int64_t nkb = cdiv(d.len_kv, C::BK);
+  a.rsplit = 1;
+  a.ws = nullptr;
+  {
+    int64_t total = 0, longest = 0;
+    for (int64_t kb = 0; kb < nkb; ++kb) {
+      const int st = dkdv_span(a, kb * C::BK, C::BK, C::BQ).steps;
+      total += st;
+      longest = std::max<int64_t>(longest, st);
+    }
+    total *= int64_t(d.heads_kv) * d.batch;
+    static int cus = 0;
+    if (cus == 0) {
+      int dev = 0;
+      hipDeviceProp_t prop;
+      cus = (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
+                ? prop.multiProcessorCount : 256;
+    }
+    const int64_t share = std::max<int64_t>(1, cdiv(total, cus));
+    int64_t split = longest > 2 * share ? cdiv(longest, share) : 1;
+    split = std::min<int64_t>({split, kMaxSplit, std::max<int64_t>(1, longest / kMinSplitSteps)});
+    const size_t per = size_t(2) * d.batch * d.len_kv * d.heads_kv * D * sizeof(float);
+    split = std::min<int64_t>(split, int64_t(kMaxSplitBytes / per));
+    if (split > 1) {
+      a.ws = split_workspace(size_t(split) * per);
+      if (a.ws != nullptr) a.rsplit = int32_t(split);
+    }
+  }
+  dim3 grid(unsigned(nkb) * unsigned(d.heads_kv), unsigned(d.batch), unsigned(a.rsplit));
   auto go = [&](auto kern) {
     const dfa_status st = allow_lds(kern, C::LDS_BYTES, "dkdv_bf16_kernel");
     if (st != DFA_OK) return st;
     hipLaunchKernelGGL(kern, grid, dim3(C::NT), C::LDS_BYTES, s, a);
     return check_launch("dkdv_bf16_kernel");
   };
-  if (pair_is_full(d, C::BK) && d.len_q % C::BQ == 0)
-    return go(dkdv_bf16_kernel<D, kDkvNW, true>);
-  return go(dkdv_bf16_kernel<D, kDkvNW, false>);
+  const dfa_status st = (pair_is_full(d, C::BK) && d.len_q % C::BQ == 0)
+                            ? go(dkdv_bf16_kernel<D, kDkvNW, true>)
+                            : go(dkdv_bf16_kernel<D, kDkvNW, false>);
+  if (st != DFA_OK || a.rsplit == 1) return st;
+  const int64_t n4 = int64_t(d.batch) * d.len_kv * d.heads_kv * D / 4;
+  hipLaunchKernelGGL((dkdv_split_reduce_kernel<C::BK, C::BQ>), dim3(unsigned(cdiv(n4, 256))),
+                     dim3(256), 0, s, a, n4, int32_t(d.heads_kv * D / 4));
+  return check_launch("dkdv_split_reduce_kernel");
 }
 
 }  // namespace
