@@ -39,7 +39,7 @@ KERNEL_NAMES = {"fwd": "fwd_bf16_kernel", "dkdv": "dkdv_bf16_kernel", "dq": "dq_
 # fp32 inputs run the exact fp32 kernels (one wave per row, vector ALU, no MFMA)
 KERNEL_NAMES_F32 = {"fwd": "fwd_f32_kernel", "dkdv": "dkdv_f32_kernel", "dq": "dq_f32_kernel"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-KERNEL_SOURCES = {"fwd_bf16_kernel": ("fwd_mfma.hip",),
+KERNEL_SOURCES = {"fwd_bf16_kernel": ("fwd_mfma.hip", "transpose.hip"),
                   "dkdv_bf16_kernel": ("dkdv_mfma.hip", "bwd_common.hpp"),
                   "dq_bf16_kernel": ("dq_mfma.hip", "bwd_common.hpp")}
 

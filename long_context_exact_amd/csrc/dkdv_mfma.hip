@@ -2,7 +2,6 @@
 // backward; see bwd_mfma.hip for the pair of kernels and their contract).
 #include <algorithm>
 #include <cfloat>
-#include <mutex>
 
 #include "bwd_common.hpp"
 
@@ -314,31 +313,6 @@ __global__ __launch_bounds__(256) void dkdv_split_reduce_kernel(BwdArgs a, int64
   dv[i] += sv;
 }
 
-// Library-owned scratch for the split partials, one buffer per device, grown
-// on demand (kept until the process ends).
-float* split_workspace(size_t bytes) {
-  static std::mutex mu;
-  static void* ptr[64] = {};
-  static size_t cap[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  std::lock_guard<std::mutex> lock(mu);
-  if (cap[dev] >= bytes) return static_cast<float*>(ptr[dev]);
-  if (ptr[dev] != nullptr) {  // work queued with the old buffer must finish first
-    if (hipDeviceSynchronize() != hipSuccess || hipFree(ptr[dev]) != hipSuccess) return nullptr;
-    ptr[dev] = nullptr;
-    cap[dev] = 0;
-  }
-  void* p = nullptr;
-  if (hipMalloc(&p, bytes) != hipSuccess) {
-    (void)hipGetLastError();
-    return nullptr;
-  }
-  ptr[dev] = p;
-  cap[dev] = bytes;
-  return static_cast<float*>(p);
-}
-
 constexpr int kDkvNW = 8;
 constexpr int kMaxSplit = 64;                                // slices per key block
 constexpr int kMinSplitSteps = 32;                           // steps per slice, at least
@@ -375,7 +349,7 @@ dfa_status launch_dkdv(const dfa_attn_desc& d, BwdArgs a, hipStream_t s) {
     const size_t per = size_t(2) * d.batch * d.len_kv * d.heads_kv * D * sizeof(float);
     split = std::min<int64_t>(split, int64_t(kMaxSplitBytes / per));
     if (split > 1) {
-      a.ws = split_workspace(size_t(split) * per);
+      a.ws = static_cast<float*>(device_workspace(size_t(split) * per));
       if (a.ws != nullptr) a.rsplit = int32_t(split);
     }
   }

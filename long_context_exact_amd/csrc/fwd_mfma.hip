@@ -19,9 +19,13 @@
 //   S^T = K Q^T        (A = K rows from LDS, B = Q fragments in VGPRs),
 //   so each lane owns one query row and the row max / sum need only its
 //   16 accumulator registers plus the lane 32 apart;
-//   O^T += V^T P^T     (A = V^T via transpose reads of the row-major V tile,
-//   B = P^T straight from the S^T accumulators: the contraction order of the
-//   keys is permuted identically on both operands, so no shuffle is needed).
+//   O^T += V^T P^T     (A = V^T rows from LDS, B = P^T straight from the S^T
+//   accumulators).  Before the kernel, V is transposed once per call into
+//   library scratch, V^T [B][Hkv][d][keys], with the keys of every 16-key
+//   group stored in the order the accumulator layout hands P^T over (bits 2
+//   and 3 of the key index swapped), so each lane's A fragment is 8
+//   consecutive elements of a V^T row: a 16-byte read instead of two
+//   transposing 8-byte reads (which move half the bytes per LDS cycle).
 // Chunk pairs in which every query sees every key (the off-diagonal pairs)
 // run a mask-free instantiation whose sub-block loop is software-pipelined:
 // the S^T of the next 32 keys is issued next to the softmax of the current
@@ -37,7 +41,8 @@ namespace {
 struct FwdArgs {
   const uint16_t* q;
   const uint16_t* k;
-  const uint16_t* v;
+  const uint16_t* vt;  // V^T [B][Hkv][d][vt_ld], keys permuted within 16-key groups
+  int64_t vt_ld;       // keys per V^T row: len_kv rounded up to a whole key tile
   float* o;
   float* lse;
   uint8_t* visits;
@@ -95,7 +100,7 @@ void fwd_bf16_kernel(FwdArgs a) {
   const int64_t q_rs = int64_t(a.hq) * D;
   const int64_t kv_rs = int64_t(a.hkv) * D;
   const uint16_t* kbase = a.k + b * a.len_kv * kv_rs + int64_t(g) * D;
-  const uint16_t* vbase = a.v + b * a.len_kv * kv_rs + int64_t(g) * D;
+  const uint16_t* vtb = a.vt + (b * a.hkv + g) * D * a.vt_ld;  // this head's V^T rows
   const int64_t row = w_lo + l32;  // this lane's query row (local index)
 
   bf16x8 qf[D / 16];
@@ -131,12 +136,12 @@ void fwd_bf16_kernel(FwdArgs a) {
     // rows past the chunk re-read its last key (their scores are masked)
     const int last_row = FULL ? BN - 1 : int(min<int64_t>(a.len_kv - 1 - key0, BN - 1));
     const uint16_t* kt_base = kbase + key0 * kv_rs;
-    const uint16_t* vt_base = vbase + key0 * kv_rs;
 #pragma unroll
     for (int i = 0; i < C::SEGS / NW; ++i) {
       const int seg = wave * (C::SEGS / NW) + i;
       tile_dma_rows<D>(Ks, seg, lane, kt_base, uint32_t(kv_rs * 2), last_row);
-      tile_dma_rows<D>(Vs, seg, lane, vt_base, uint32_t(kv_rs * 2), last_row);
+      // V^T tile: D rows of BN keys (zero past the chunk's end)
+      tile_dma_rows<BN>(Vs, seg, lane, vtb + key0, uint32_t(a.vt_ld * 2), D - 1);
     }
   };
 
@@ -182,11 +187,11 @@ void fwd_bf16_kernel(FwdArgs a) {
       bf16x8 pb;
 #pragma unroll
       for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(p[8 * j + e]);
-      const int r0 = kb * 32 + 16 * j + 4 * hi;
+      // lane (d, hi) takes keys kb*32 + 16j + 4hi + {0..3, 8..11}: positions
+      // 8hi..8hi+7 of the 16-key group in V^T's permuted order
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const int c0 = 32 * db + 16 * half16;
-        const bf16x8 va = cat4(tile_tr4<D>(Vs, r0, c0, lane), tile_tr4<D>(Vs, r0 + 8, c0, lane));
+        const bf16x8 va = tile_row8<BN>(Vs, 32 * db + l32, 4 * kb + 2 * j + hi);
         oacc[db] = mfma32(va, pb, oacc[db]);
       }
     }
@@ -341,7 +346,6 @@ dfa_status launch_fwd(const dfa_attn_desc& d, const void* q, const void* k, cons
   FwdArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v);
   a.o = o;
   a.lse = lse;
   a.visits = visits;
@@ -358,6 +362,21 @@ dfa_status launch_fwd(const dfa_attn_desc& d, const void* q, const void* k, cons
   // every visible key the weight exp2(0) = 1 in fp32.
   a.c = std::max(d.scale * kLog2e, FLT_MIN);
   a.win = d.window > 0 ? d.window : kNoWindow;
+  // V^T into library scratch (stream-ordered before the forward kernel)
+  a.vt_ld = cdiv(d.len_kv, kBN) * kBN;
+  if (uint64_t(a.vt_ld) * 2 * uint64_t(d.head_dim) >= (uint64_t(1) << 32))
+    return fail(DFA_ERR_UNSUPPORTED, "dfa_attn_fwd_partial: len_kv too large for 32-bit V^T offsets");
+  if (a.vt_ld > 0) {
+    const size_t bytes = size_t(d.batch) * d.heads_kv * d.head_dim * size_t(a.vt_ld) * 2;
+    uint16_t* vt = static_cast<uint16_t*>(device_workspace(bytes));
+    if (vt == nullptr)
+      return fail(DFA_ERR_HIP, "dfa_attn_fwd_partial: cannot allocate " + std::to_string(bytes) +
+                                   " bytes of V^T scratch");
+    const dfa_status st = launch_kv_transpose(static_cast<const uint16_t*>(v), vt, d.batch,
+                                              d.len_kv, d.heads_kv, d.head_dim, a.vt_ld, s);
+    if (st != DFA_OK) return st;
+    a.vt = vt;
+  }
   if (d.head_dim == 128) return launch_d<128>(d, a, visits != nullptr, s);
   return launch_d<64>(d, a, visits != nullptr, s);
 }

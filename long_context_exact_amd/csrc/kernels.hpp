@@ -52,6 +52,17 @@ inline bool pair_is_full(const dfa_attn_desc& d, int64_t tile) {
   return all_visible && in_window && d.len_kv % tile == 0;
 }
 
+// Library-owned device scratch of at least `bytes` (one buffer per device,
+// shared by every call on it: calls that use it must be stream-ordered);
+// nullptr if it cannot be allocated.
+void* device_workspace(size_t bytes);
+
+// X [B][len][H][d] bf16 -> X^T [B][H][d][ld] (ld a multiple of 64, >= len):
+// keys permuted within 16-key groups (index bits 2 and 3 swapped), keys past
+// len zero.  The layout the forward reads V^T from for O^T += V^T P^T.
+dfa_status launch_kv_transpose(const uint16_t* x, uint16_t* xt, int32_t batch, int64_t len,
+                               int32_t heads, int32_t head_dim, int64_t ld, hipStream_t s);
+
 // o = 0, lse = -inf for every row (a chunk pair with no keys).
 dfa_status launch_fill_empty(int64_t n_o, float* o, int64_t n_lse, float* lse,
                              hipStream_t s);
