@@ -31,7 +31,8 @@ struct DkvCfg {
   static_assert(LDS_BYTES <= 160 * 1024, "fits gfx950 LDS");
 };
 
-template <int D, int NW, bool FULL>
+// TM: tile-major step order (see tile_of below), for pairs without a window.
+template <int D, int NW, bool FULL, bool TM>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DFA_BWD_OCC, DFA_BWD_OCC)))
 void dkdv_bf16_kernel(BwdArgs a) {
   using C = DkvCfg<D, NW>;
@@ -64,6 +65,16 @@ void dkdv_bf16_kernel(BwdArgs a) {
   const int it0 = int(blockIdx.z) * per;
   const int it1 = min(sp.steps, it0 + per);
   if (it0 >= it1) return;  // the reduction skips slices without steps
+  // Step it covers query tile tile_of(it) of head head_of(it).  Without a
+  // window every key block's rows end at the chunk's end: tiles run from the
+  // last one down with the group's heads innermost, so the workgroups running
+  // side by side read the same Q / dO tile at the same time (until each
+  // reaches its own first row) and share it in L2 (a diagonal pair's HBM
+  // reads drop several-fold).  With a window the row ranges slide with the
+  // key block: heads outermost, tiles ascending, keeps neighbouring blocks a
+  // few steps apart in the same head's rows instead.
+  auto tile_of = [&](int it) { return TM ? qt0 + nq - 1 - it / a.group : qt0 + it % nq; };
+  auto head_of = [&](int it) { return g * a.group + (TM ? it % a.group : it / nq); };
 
   // K of this lane's key as the B operand of S (elements d = 16*st + 8*hi
   // + e), in VGPRs for the whole loop; V rows of the workgroup in LDS.
@@ -92,8 +103,8 @@ void dkdv_bf16_kernel(BwdArgs a) {
 
   auto stage_ptr = [&](int stage) { return smem + C::KV_TILE + stage * C::STAGE; };
   auto stage_q = [&](int it, int stage) {
-    const int h = g * a.group + it / nq;
-    const int64_t i0 = int64_t(qt0 + it % nq) * C::BQ;
+    const int h = head_of(it);
+    const int64_t i0 = int64_t(tile_of(it)) * C::BQ;
     const uint16_t* qb = a.q + b * a.len_q * q_rs + int64_t(h) * D;
     const uint16_t* db_ = a.d_o + b * a.len_q * q_rs + int64_t(h) * D;
     lds_u16* Qs = stage_ptr(stage);
@@ -126,8 +137,8 @@ void dkdv_bf16_kernel(BwdArgs a) {
   float raw_l = 0.f, raw_d = 0.f;
   bool raw_ok = false;
   auto load_stats = [&](int it) {
-    const int h = g * a.group + it / nq;
-    const int64_t row = int64_t(qt0 + it % nq) * C::BQ + lane;
+    const int h = head_of(it);
+    const int64_t row = int64_t(tile_of(it)) * C::BQ + lane;
     raw_ok = lane < C::BQ && (FULL || row < a.len_q);
     const int64_t li = (b * a.hq + h) * a.len_q + min<int64_t>(row, a.len_q - 1);
     raw_l = a.lse[li];
@@ -161,7 +172,7 @@ void dkdv_bf16_kernel(BwdArgs a) {
     const lds_u16* Qs = stage_ptr(stage);
     const lds_u16* dOs = Qs + C::Q_TILE;
     const lds_f32* stats = reinterpret_cast<const lds_f32*>(Qs + 2 * C::Q_TILE);
-    const int64_t r0 = int64_t(qt0 + it % nq) * C::BQ;  // first row of this step
+    const int64_t r0 = int64_t(tile_of(it)) * C::BQ;  // first row of this step
     bool any = wave_active;
     if constexpr (!FULL) {
       if (any && a.causal) any = a.q_start + min<int64_t>(r0 + C::BQ, a.len_q) - 1 >= a.kv_start + wk_lo;
@@ -360,9 +371,11 @@ dfa_status launch_dkdv(const dfa_attn_desc& d, BwdArgs a, hipStream_t s) {
     hipLaunchKernelGGL(kern, grid, dim3(C::NT), C::LDS_BYTES, s, a);
     return check_launch("dkdv_bf16_kernel");
   };
+  // a fully visible pair's key blocks all run the same rows: tile-major order
   const dfa_status st = (pair_is_full(d, C::BK) && d.len_q % C::BQ == 0)
-                            ? go(dkdv_bf16_kernel<D, kDkvNW, true>)
-                            : go(dkdv_bf16_kernel<D, kDkvNW, false>);
+                            ? go(dkdv_bf16_kernel<D, kDkvNW, true, true>)
+                        : d.window <= 0 ? go(dkdv_bf16_kernel<D, kDkvNW, false, true>)
+                                        : go(dkdv_bf16_kernel<D, kDkvNW, false, false>);
   if (st != DFA_OK || a.rsplit == 1) return st;
   const int64_t n4 = int64_t(d.batch) * d.len_kv * d.heads_kv * D / 4;
   hipLaunchKernelGGL((dkdv_split_reduce_kernel<C::BK, C::BQ>), dim3(unsigned(cdiv(n4, 256))),
