@@ -144,7 +144,12 @@ dfa_status dfa_global_window_schedule(int32_t num_workers, int64_t chunk_len,
  *   overwritten.  Only the causal prefix is computed: key tiles entirely
  *   after a query tile's last row are skipped (§2, §3.2), and with a
  *   window so are key tiles entirely outside every window of the tile's
- *   rows (App. F). */
+ *   rows (App. F).  For bf16 inputs the call first writes a transposed copy
+ *   of v into a scratch buffer the library allocates once per device (grown
+ *   on demand, kept until the process ends; growing it synchronizes the
+ *   device).  Every call that uses that buffer (this one, and dfa_attn_bwd
+ *   when it splits rows) must be ordered against the others on one device:
+ *   issue them on one stream. */
 dfa_status dfa_attn_fwd_partial(const dfa_attn_desc* desc, const void* q,
                                 const void* k, const void* v, float* o_part,
                                 float* lse, void* hip_stream);
@@ -185,9 +190,9 @@ dfa_status dfa_lse_merge(int32_t n, const float* const* o_parts,
  * window band) the dK/dV part splits each block's rows over several
  * workgroups and sums their partials in a fixed order, in a scratch buffer
  * the library allocates once per device (grown on demand, kept until the
- * process ends; growing it synchronizes the device).  Calls that split share
- * that buffer: on one device they must not run concurrently (issue them on
- * one stream); calls on one stream are ordered. */
+ * process ends; growing it synchronizes the device), the same buffer
+ * dfa_attn_fwd_partial uses: on one device such calls must not run
+ * concurrently (issue them on one stream); calls on one stream are ordered. */
 dfa_status dfa_attn_bwd(const dfa_attn_desc* desc, const void* q,
                         const void* k, const void* v, const void* o,
                         const float* lse, const void* d_o, float* delta,
