@@ -46,7 +46,8 @@ extern "C" {
 typedef enum {
   DFA_OK = 0,
   DFA_ERR_INVALID = 1,      /* malformed argument (null pointer, bad shape) */
-  DFA_ERR_UNSUPPORTED = 2,  /* well-formed but not implemented (head_dim)   */
+  DFA_ERR_UNSUPPORTED = 2,  /* well-formed but not implemented (head_dim, */
+                            /* head counts past the 32-bit tile offsets)  */
   DFA_ERR_CAPACITY = 3,     /* output array too small; required size given  */
   DFA_ERR_HIP = 4           /* the HIP runtime reported an error            */
 } dfa_status;
@@ -67,7 +68,8 @@ typedef struct {
 /* Shape and masking of one (query chunk, key/value chunk) pair. */
 typedef struct {
   int32_t batch;        /* >= 1                                            */
-  int32_t heads_q;      /* >= 1, a multiple of heads_kv                    */
+  int32_t heads_q;      /* >= 1, a multiple of heads_kv; heads_q *       */
+                        /* head_dim < 2^21 (else DFA_ERR_UNSUPPORTED)     */
   int32_t heads_kv;     /* >= 1                                            */
   int32_t head_dim;     /* 64 or 128 (else DFA_ERR_UNSUPPORTED)            */
   int64_t len_q;        /* query rows in the chunk, >= 0, any value        */

@@ -347,13 +347,11 @@ dfa_status launch_dkdv(const dfa_attn_desc& d, BwdArgs a, hipStream_t s) {
       longest = std::max<int64_t>(longest, st);
     }
     total *= int64_t(d.heads_kv) * d.batch;
-    static int cus = 0;
-    if (cus == 0) {
-      int dev = 0;
-      hipDeviceProp_t prop;
-      cus = (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
-                ? prop.multiProcessorCount : 256;
-    }
+    int dev = 0, cus = 0;  // the current device's compute units (a cheap attribute query)
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
     const int64_t share = std::max<int64_t>(1, cdiv(total, cus));
     int64_t split = longest > 2 * share ? cdiv(longest, share) : 1;
     split = std::min<int64_t>({split, kMaxSplit, std::max<int64_t>(1, longest / kMinSplitSteps)});

@@ -133,6 +133,7 @@ def _fwd(L, d, q=FAKE, o=FAKE, lse=FAKE):
     ("dtype", 7, D.DFA_ERR_INVALID),
     ("batch", -1, D.DFA_ERR_INVALID),
     ("window", -1, D.DFA_ERR_INVALID),
+    ("heads_q", 16384, D.DFA_ERR_UNSUPPORTED),  # 16384 * 128 = 2^21: past 32-bit tile offsets
 ])
 def test_fwd_descriptor_errors(dfa_lib, field, value, status):
     L = dfa_lib.lib()
