@@ -126,6 +126,10 @@ def _ptr(t, name, shape, dtype):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    if t.device.index is not None and t.device.index != torch.cuda.current_device():
+        # the library launches on the current device
+        raise ValueError(f"{name} is on {t.device}, but the current device is "
+                         f"cuda:{torch.cuda.current_device()}")
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if t.dtype != dtype:
