@@ -132,3 +132,74 @@ def test_pair_past_2_31_elements():
             assert rel_fro(gk, rk[0, :, 0]) <= 2e-2, f"dK head {h} keys {k0}..: {rel_fro(gk, rk[0, :, 0])}"
             assert rel_fro(gv, rv[0, :, 0]) <= 2e-2, f"dV head {h} keys {k0}..: {rel_fro(gv, rv[0, :, 0])}"
             assert np.abs(gv).max() > 0
+
+
+def _rows_bits(seed, heads):
+    """[LQL, heads, DH] bf16 bits, built like _kv_bits over the query axis."""
+    base = bf16_bits(bf16_round(
+        np.random.default_rng(seed).standard_normal((LQL, DH), dtype=np.float32)))
+    out = np.empty((LQL, heads, DH), dtype=np.uint16)
+    for h in range(heads):
+        s = 991 * h
+        out[s:, h, :] = base[:LQL - s]
+        out[:s, h, :] = base[LQL - s:]
+    return out
+
+
+LQL = (1 << 21) + 4099  # query rows: LQL * 8 * 128 > 2^31 elements of Q, dO, O, dQ
+LKS = 300               # keys, at the last 300 positions of the query range
+HQ, HKV = 8, 2          # grouped query heads, 4 per key/value head
+
+
+def test_pair_past_2_31_query_elements():
+    """The query side past 2^31 elements: the keys sit at the last LKS
+    positions, so rows before them see nothing (O = 0, LSE = -inf) and the
+    last LKS rows, all past the mark, see a causal prefix of them; dK and dV
+    then depend on those rows only and are checked exactly."""
+    print(f"case large query pair LQ={LQL} LK={LKS} HQ={HQ} HKV={HKV} d={DH}", flush=True)
+    qb, dob = _rows_bits(21, HQ), _rows_bits(22, HQ)
+    rng = np.random.default_rng(23)
+    k = rand(rng, (1, LKS, HKV, DH), "bf16")
+    v = rand(rng, (1, LKS, HKV, DH), "bf16")
+    scale = DH ** -0.5
+    k0 = LQL - LKS  # kv_start, with q_start = 0
+    tail = slice(LQL - LKS, LQL)
+
+    def rows(bits, sl, h0, h1):
+        x = (bits[sl, h0:h1, :].astype(np.uint32) << np.uint32(16)).view(np.float32)
+        return x.astype(np.float64)[None]
+
+    q_d = torch.from_numpy(qb).to(DEV).view(torch.bfloat16)[None]
+    do_d = torch.from_numpy(dob).to(DEV).view(torch.bfloat16)[None]
+    k_d, v_d = (torch.from_numpy(x).to(DEV).to(torch.bfloat16) for x in (k, v))
+    desc = D.make_desc(1, HQ, HKV, DH, LQL, LKS, 0, k0, True, scale, "bf16")
+    o_part = torch.empty(1, LQL, HQ, DH, device=DEV)
+    lse = torch.empty(1, HQ, LQL, device=DEV)
+    D.dfa_attn_fwd_partial(desc, q_d, k_d, v_d, o_part, lse)
+    torch.cuda.synchronize()
+    # rows before the keys see nothing
+    assert torch.all(o_part[:, :k0] == 0) and torch.all(lse[:, :, :k0] == -float("inf"))
+    # the last rows, every head, against the oracle
+    qt, dot = rows(qb, tail, 0, HQ), rows(dob, tail, 0, HQ)
+    ro, rl = oracle.attention_fwd(qt, k, v, scale, True, LQL - LKS, k0)
+    check_o(o_part[:, tail].cpu().numpy().astype(np.float64), ro, "bf16", "O tail")
+    check_lse(lse[:, :, tail].cpu().numpy().astype(np.float64), rl, "bf16", "LSE tail")
+
+    # backward from the saved output: the oracle's O (in bf16) and LSE on the
+    # rows that see keys, O = 0 and LSE = -inf before them
+    o_in = torch.zeros(1, LQL, HQ, DH, device=DEV, dtype=torch.bfloat16)
+    o_in[:, tail] = torch.from_numpy(bf16_round(ro.astype(np.float32))).to(DEV).to(torch.bfloat16)
+    lse_in = torch.full((1, HQ, LQL), -float("inf"), device=DEV)
+    lse_in[:, :, tail] = torch.from_numpy(rl.astype(np.float32)).to(DEV)
+    delta = torch.empty(1, HQ, LQL, device=DEV)
+    dq = torch.zeros(1, LQL, HQ, DH, device=DEV)
+    dk = torch.zeros(1, LKS, HKV, DH, device=DEV)
+    dv = torch.zeros(1, LKS, HKV, DH, device=DEV)
+    D.dfa_attn_bwd(desc, q_d, k_d, v_d, o_in, lse_in, do_d, delta, True, dq, dk, dv)
+    torch.cuda.synchronize()
+    assert torch.all(dq[:, :k0] == 0)
+    o_t = o_in[:, tail].float().cpu().numpy().astype(np.float64)
+    rq, rk, rv = oracle.attention_bwd(qt, k, v, o_t, rl, dot, scale, True, LQL - LKS, k0)
+    check_grad(dq[:, tail].cpu().numpy().astype(np.float64), rq, "bf16", "dQ tail")
+    check_grad(dk.cpu().numpy().astype(np.float64), rk, "bf16", "dK")
+    check_grad(dv.cpu().numpy().astype(np.float64), rv, "bf16", "dV")
