@@ -155,7 +155,8 @@ def test_pair_past_2_31_query_elements():
     """The query side past 2^31 elements: the keys sit at the last LKS
     positions, so rows before them see nothing (O = 0, LSE = -inf) and the
     last LKS rows, all past the mark, see a causal prefix of them; dK and dV
-    then depend on those rows only and are checked exactly."""
+    then depend on those rows only and are checked exactly.  The LSE merge
+    of two partials over halves of the keys runs over the same rows."""
     print(f"case large query pair LQ={LQL} LK={LKS} HQ={HQ} HKV={HKV} d={DH}", flush=True)
     qb, dob = _rows_bits(21, HQ), _rows_bits(22, HQ)
     rng = np.random.default_rng(23)
@@ -184,6 +185,28 @@ def test_pair_past_2_31_query_elements():
     ro, rl = oracle.attention_fwd(qt, k, v, scale, True, LQL - LKS, k0)
     check_o(o_part[:, tail].cpu().numpy().astype(np.float64), ro, "bf16", "O tail")
     check_lse(lse[:, :, tail].cpu().numpy().astype(np.float64), rl, "bf16", "LSE tail")
+
+    # the LSE merge over the same rows: two partials over disjoint halves of
+    # the keys merge to the whole (rows that see neither half stay O = 0,
+    # LSE = -inf)
+    parts = []
+    for a0, a1 in ((0, LKS // 2), (LKS // 2, LKS)):
+        dsc = D.make_desc(1, HQ, HKV, DH, LQL, a1 - a0, 0, k0 + a0, True, scale, "bf16")
+        op = torch.empty(1, LQL, HQ, DH, device=DEV)
+        lp = torch.empty(1, HQ, LQL, device=DEV)
+        D.dfa_attn_fwd_partial(dsc, q_d, k_d[:, a0:a1].contiguous(), v_d[:, a0:a1].contiguous(),
+                               op, lp)
+        parts.append((op, lp))
+    o_m = torch.empty(1, LQL, HQ, DH, device=DEV, dtype=torch.bfloat16)
+    l_m = torch.empty(1, HQ, LQL, device=DEV)
+    D.dfa_lse_merge([x[0] for x in parts], [x[1] for x in parts], 1, HQ, LQL, DH, "bf16", o_m, l_m)
+    torch.cuda.synchronize()
+    del parts
+    assert torch.all(o_m[:, :k0] == 0) and torch.all(l_m[:, :, :k0] == -float("inf"))
+    check_o(o_m[:, tail].float().cpu().numpy().astype(np.float64), ro, "bf16", "merged O tail",
+            stored_bf16=True)
+    check_lse(l_m[:, :, tail].cpu().numpy().astype(np.float64), rl, "bf16", "merged LSE tail")
+    del o_m, l_m
 
     # backward from the saved output: the oracle's O (in bf16) and LSE on the
     # rows that see keys, O = 0 and LSE = -inf before them
