@@ -213,7 +213,7 @@ def main():
         copy_calibration(args.copy_gib)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the schedule's "
+        print("bench.py measures one GPU: the library has no multi-GPU path (the schedule's "
               "workers are emulated as work items on one device); run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
