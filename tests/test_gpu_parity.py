@@ -196,6 +196,9 @@ def test_special_cases_constant_v_zero_q_peaky():
 @pytest.mark.parametrize("lq,lk,q0,k0,hq,hkv", [
     (1000, 1000, 0, 0, 4, 4), (1000, 1000, 0, 0, 64, 8), (300, 500, 4096, 0, 4, 2),
     (257, 257, 257, 257, 2, 2), (96, 300, 200, 0, 4, 1),
+    # a tile whose last key is exactly its first query (visited whole, unmasked):
+    # 32 x 128 tiles (grouped heads) and 256 x 128 tiles (one head per kv head)
+    (300, 400, 127, 0, 64, 8), (600, 700, 383, 0, 4, 4),
 ])
 def test_tile_visit_map_bit_exact(lq, lk, q0, k0, hq, hkv):
     print(f"case tiles {lq} {lk} {q0} {k0} {hq} {hkv}", flush=True)

@@ -113,6 +113,8 @@ def test_windowed_pair(lq, lk, q0, k0, win, dtype):
 @pytest.mark.parametrize("lq,lk,q0,k0,hq,hkv,win", [
     (1000, 1000, 0, 0, 4, 4, 300), (1000, 1000, 1000, 0, 64, 8, 700),
     (300, 500, 4096, 3700, 4, 2, 500), (257, 257, 257, 257, 2, 2, 40), (96, 300, 200, 0, 4, 1, 150),
+    # tile (10, 0) of 32 x 128 tiles: its closest pair is exactly `win` apart (skipped)
+    (600, 600, 0, 0, 64, 8, 193),
 ])
 def test_windowed_tile_visit_map_bit_exact(lq, lk, q0, k0, hq, hkv, win):
     print(f"case window tiles {lq} {lk} {q0} {k0} {hq} {hkv} {win}", flush=True)

@@ -116,6 +116,8 @@ def _tile_map_by_elements(lq, lk, q0, k0, causal, bm, bn):
     (64, 64, 0, 0, True, 16, 16), (70, 50, 0, 0, True, 16, 32), (33, 90, 40, 7, True, 8, 16),
     (40, 40, 100, 0, True, 16, 16), (40, 40, 0, 100, True, 16, 16), (37, 23, 0, 0, False, 8, 8),
     (100, 100, 0, 0, True, 32, 64),
+    # tiles whose last key is exactly their first query (visible whole, no mask)
+    (64, 64, 15, 0, True, 16, 16), (48, 64, 31, 0, True, 16, 32),
 ])
 def test_tile_map_matches_element_enumeration(case):
     assert np.array_equal(causal_tile_map(*case), _tile_map_by_elements(*case))

@@ -223,8 +223,10 @@ def test_schedule_worker_7_of_8_visits_chunks_6_and_7():
 
 
 def test_tile_map_matches_element_enumeration():
+    # the last case has tiles whose closest pair is exactly `win` apart (not visited)
     for (lq, lk, q0, k0, bm, bn, win) in [(64, 64, 0, 0, 16, 8, 20), (40, 48, 48, 0, 8, 16, 30),
-                                          (32, 32, 64, 0, 8, 8, 40), (33, 47, 50, 3, 8, 16, 11)]:
+                                          (32, 32, 64, 0, 8, 8, 40), (33, 47, 50, 3, 8, 16, 11),
+                                          (64, 64, 0, 0, 16, 8, 25)]:
         m = causal_tile_map(lq, lk, q0, k0, True, bm, bn, window=win)
         for qt in range(m.shape[0]):
             for kt in range(m.shape[1]):
