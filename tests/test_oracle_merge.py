@@ -93,3 +93,24 @@ def test_far_apart_lse_values():
     mo, ml = lse_merge([o1, o2], [l1, l2])
     assert np.max(np.abs(mo - o1)) <= 1e-15
     assert np.max(np.abs(ml - 400.0)) <= 1e-13
+
+
+def test_rows_every_part_leaves_empty():
+    """Rows whose every partial saw no key (LSE = -inf everywhere) merge to
+    O = 0 and LSE = -inf; the other rows are merged as usual."""
+    o1 = RNG.standard_normal((1, 4, 2, 3))
+    o2 = RNG.standard_normal((1, 4, 2, 3))
+    l1 = RNG.standard_normal((1, 2, 4))
+    l2 = RNG.standard_normal((1, 2, 4))
+    for lx in (l1, l2):
+        lx[0, 1, 2] = -np.inf        # head 1, row 2: empty in every part
+    o1[0, 2, 1] = 0.0
+    o2[0, 2, 1] = 0.0
+    mo, ml = lse_merge([o1, o2], [l1, l2])
+    assert ml[0, 1, 2] == -np.inf and np.all(mo[0, 2, 1] == 0.0)
+    assert np.all(np.isfinite(np.delete(ml.reshape(-1), 1 * 4 + 2)))
+    # a live row: both parts weighted by their share of the union's mass
+    lse = np.logaddexp(l1[0, 0, 0], l2[0, 0, 0])
+    assert abs(ml[0, 0, 0] - lse) <= 1e-14
+    want = np.exp(l1[0, 0, 0] - lse) * o1[0, 0, 0] + np.exp(l2[0, 0, 0] - lse) * o2[0, 0, 0]
+    assert np.max(np.abs(mo[0, 0, 0] - want)) <= 1e-14

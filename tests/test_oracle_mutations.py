@@ -75,6 +75,27 @@ MUTATIONS = [
     ("global schedule keeps the empty chunk-0 pair", "schedule.py",
      "items = [it for it in items if not (it[3] == 0 and g == c)]", "items = list(items)",
      ["global"]),
+    ("row maximum taken as the minimum", "attention.py",
+     "m = s.max(axis=1)", "m = s.min(axis=1)", ["fwd"]),
+    ("rows without keys get LSE 0", "attention.py",
+     "lse = np.full((b, hq, lq), -np.inf, dtype=np.float64)",
+     "lse = np.full((b, hq, lq), 0.0, dtype=np.float64)", ["fwd"]),
+    ("merge treats rows that every part leaves empty as live", "attention.py",
+     "live = np.isfinite(m)\n    m_safe", "live = np.ones_like(m, dtype=bool)\n    m_safe",
+     ["merge"]),
+    ("one worker's global item missing", "schedule.py",
+     "items += [(0, w, w, -1, GLOBAL, w) for w in range(p)]",
+     "items += [(0, w, w, -1, GLOBAL, w) for w in range(1, p)]", ["global"]),
+    ("window schedule skips the first worker of a step", "schedule.py",
+     "for w in range(t, p):", "for w in range(t + 1, p):", ["window"]),
+    ("balanced schedule one step short", "schedule.py",
+     "steps = 1 + p // 2", "steps = p // 2", ["schedule"]),
+    ("unbalanced schedule calls the diagonal pair full", "schedule.py",
+     "items.append((t, w, w, w - t, DIAG if t == 0 else FULL, w))",
+     "items.append((t, w, w, w - t, FULL, w))", ["schedule"]),
+    ("non-causal tile map marks tiles masked", "schedule.py",
+     "            if not causal:\n                out[qt, kt] = 1",
+     "            if not causal:\n                out[qt, kt] = 2", ["schedule"]),
 ]
 
 
