@@ -13,6 +13,7 @@ import inspect
 import os
 import sys
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -134,7 +135,8 @@ def _first_failing_pin(pins):
         for fn in tests:
             for kw in _cases(fn):
                 try:
-                    fn(**kw)
+                    with np.errstate(all="ignore"):  # a mutant may produce NaN or inf
+                        fn(**kw)
                 except Exception:  # an assertion, or any error the mistake causes
                     return f"{mod.__name__}::{fn.__name__}{kw or ''}"
     return None
