@@ -31,12 +31,15 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "causal attn fwd+bwd TFLOP/s (1 GPU) at 32K chunk; % of bf16 MFMA peak"
-PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # MI355X dense MFMA peaks
+# Peaks of the arithmetic each input dtype runs in on MI355X: bf16 inputs on
+# dense bf16 MFMA; fp32 inputs on the exact path, fp64 on the vector ALU.
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 78.6}
+ARITH_DTYPE = {"bf16": "bf16", "f32": "f64"}
 
 
 # Profiler names of the kernels the default build launches for bf16 head_dim 128.
 KERNEL_NAMES = {"fwd": "fwd_bf16_kernel", "dkdv": "dkdv_bf16_kernel", "dq": "dq_bf16_kernel"}
-# fp32 inputs run the exact fp32 kernels (one wave per row, vector ALU, no MFMA)
+# fp32 inputs run the exact kernels (one wave per row, fp64 on the vector ALU, no MFMA)
 KERNEL_NAMES_F32 = {"fwd": "fwd_f32_kernel", "dkdv": "dkdv_f32_kernel", "dq": "dq_f32_kernel"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = {"fwd_bf16_kernel": ("fwd_mfma.hip", "transpose.hip"),
@@ -352,7 +355,7 @@ def main():
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": w.dtype, "data": "synthetic",
+        "dtype": ARITH_DTYPE[w.dtype], "data": "synthetic",
         "pct_of_peak": round(100 * tflops / peak, 2),
         "median_ms_per_step": round(median_ms, 3),
         "median_value": round(flop / (median_ms * 1e-3) / 1e12, 2),

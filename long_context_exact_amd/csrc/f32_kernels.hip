@@ -3,15 +3,18 @@
 // These kernels carry the fp32 workloads, whose tolerance (1e-5 absolute
 // against float64) rules out bf16 MFMA.  One wave owns one query row (or
 // one key row in the dK/dV kernel); lanes split head_dim, dot products are
-// wave reductions, and every score is accumulated in fp32 with the precise
-// exp/log.  Same semantics as the MFMA path: causal prefix only, partial O
-// plus natural-log LSE, backward from the saved O and LSE.
+// wave reductions.  Inputs and outputs are fp32, but scores, exponentials
+// and every sum are carried in fp64: a gradient summed over a head group
+// and a few hundred rows in fp32 drifts past 1e-5 once it reaches ~10, while
+// in fp64 only the final rounding to fp32 remains.  Same semantics as the
+// MFMA path: causal prefix only, partial O plus natural-log LSE, backward
+// from the saved O and LSE.
 #include "kernels.hpp"
 
 namespace dfa {
 namespace {
 
-__device__ __forceinline__ float wave_sum(float x) {
+__device__ __forceinline__ double wave_sum(double x) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
   return x;
@@ -44,10 +47,10 @@ struct Row {
 #pragma unroll
     for (int i = 0; i < D / 64; ++i) x[i] = p[lane + 64 * i];
   }
-  __device__ float dot(const Row& o) const {
-    float s = 0.f;
+  __device__ double dot(const Row& o) const {
+    double s = 0.0;
 #pragma unroll
-    for (int i = 0; i < D / 64; ++i) s += x[i] * o.x[i];
+    for (int i = 0; i < D / 64; ++i) s += double(x[i]) * double(o.x[i]);
     return wave_sum(s);
   }
 };
@@ -76,25 +79,26 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(F32Args a) {
   q.load(a.q + (b * a.len_q + row) * q_rs + int64_t(h) * D, lane);
   const float* kb = a.k + b * a.len_kv * kv_rs + int64_t(g) * D;
   const float* vb = a.v + b * a.len_kv * kv_rs + int64_t(g) * D;
-  float m = -INFINITY, l = 0.f, acc[D / 64] = {};
+  double m = -INFINITY, l = 0.0, acc[D / 64] = {};
   const int64_t nk = visible_keys(a, row);
   for (int64_t j = first_key(a, row); j < nk; ++j) {
     Row<D> k, v;
     k.load(kb + j * kv_rs, lane);
     v.load(vb + j * kv_rs, lane);
-    const float s = a.scale * q.dot(k);
-    const float m_new = fmaxf(m, s);
-    const float alpha = expf(m - m_new);  // m = -inf on the first key -> 0
-    const float p = expf(s - m_new);
+    const double s = double(a.scale) * q.dot(k);
+    const double m_new = fmax(m, s);
+    const double alpha = exp(m - m_new);  // m = -inf on the first key -> 0
+    const double p = exp(s - m_new);
     l = l * alpha + p;
 #pragma unroll
-    for (int i = 0; i < D / 64; ++i) acc[i] = acc[i] * alpha + p * v.x[i];
+    for (int i = 0; i < D / 64; ++i) acc[i] = acc[i] * alpha + p * double(v.x[i]);
     m = m_new;
   }
   float* orow = a.out_o + (b * a.len_q + row) * q_rs + int64_t(h) * D;
 #pragma unroll
-  for (int i = 0; i < D / 64; ++i) orow[lane + 64 * i] = l > 0.f ? acc[i] / l : 0.f;
-  if (lane == 0) a.out_lse[(b * a.hq + h) * a.len_q + row] = l > 0.f ? m + logf(l) : -INFINITY;
+  for (int i = 0; i < D / 64; ++i) orow[lane + 64 * i] = l > 0.0 ? float(acc[i] / l) : 0.f;
+  if (lane == 0)
+    a.out_lse[(b * a.hq + h) * a.len_q + row] = l > 0.0 ? float(m + log(l)) : -INFINITY;
 }
 
 // dQ of one query row: sum over visible keys of dS_ij K_j.
@@ -115,20 +119,20 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(F32Args a) {
   dO.load(a.d_o + (b * a.len_q + row) * q_rs + int64_t(h) * D, lane);
   const float* kb = a.k + b * a.len_kv * kv_rs + int64_t(g) * D;
   const float* vb = a.v + b * a.len_kv * kv_rs + int64_t(g) * D;
-  float acc[D / 64] = {};
+  double acc[D / 64] = {};
   const int64_t nk = visible_keys(a, row);
   for (int64_t j = first_key(a, row); j < nk; ++j) {
     Row<D> k, v;
     k.load(kb + j * kv_rs, lane);
     v.load(vb + j * kv_rs, lane);
-    const float p = expf(a.scale * q.dot(k) - lse);
-    const float ds = p * (dO.dot(v) - dl);
+    const double p = exp(double(a.scale) * q.dot(k) - double(lse));
+    const double ds = p * (dO.dot(v) - double(dl));
 #pragma unroll
-    for (int i = 0; i < D / 64; ++i) acc[i] += ds * k.x[i];
+    for (int i = 0; i < D / 64; ++i) acc[i] += ds * double(k.x[i]);
   }
   float* out = a.dq + (b * a.len_q + row) * q_rs + int64_t(h) * D;
 #pragma unroll
-  for (int i = 0; i < D / 64; ++i) out[lane + 64 * i] += a.scale * acc[i];
+  for (int i = 0; i < D / 64; ++i) out[lane + 64 * i] += float(double(a.scale) * acc[i]);
 }
 
 // dK, dV of one key row of one key/value head: sum over the heads of its
@@ -148,7 +152,7 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(F32Args a) {
   if (a.causal) i0 = max<int64_t>(0, a.kv_start + j - a.q_start);
   // rows past the last one whose window reaches key j
   const int64_t i1 = min<int64_t>(a.len_q, a.kv_start + j + a.win - a.q_start);
-  float dk[D / 64] = {}, dv[D / 64] = {};
+  double dk[D / 64] = {}, dv[D / 64] = {};
   for (int hh = 0; hh < a.group; ++hh) {
     const int h = g * a.group + hh;
     for (int64_t i = i0; i < i1; ++i) {
@@ -157,12 +161,12 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(F32Args a) {
       Row<D> q, dO;
       q.load(a.q + (b * a.len_q + i) * q_rs + int64_t(h) * D, lane);
       dO.load(a.d_o + (b * a.len_q + i) * q_rs + int64_t(h) * D, lane);
-      const float p = expf(a.scale * q.dot(k) - lse);
-      const float ds = p * (dO.dot(v) - a.delta[(b * a.hq + h) * a.len_q + i]);
+      const double p = exp(double(a.scale) * q.dot(k) - double(lse));
+      const double ds = p * (dO.dot(v) - double(a.delta[(b * a.hq + h) * a.len_q + i]));
 #pragma unroll
       for (int t = 0; t < D / 64; ++t) {
-        dv[t] += p * dO.x[t];
-        dk[t] += ds * q.x[t];
+        dv[t] += p * double(dO.x[t]);
+        dk[t] += ds * double(q.x[t]);
       }
     }
   }
@@ -170,8 +174,8 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(F32Args a) {
   float* ov = a.dv + (b * a.len_kv + j) * kv_rs + int64_t(g) * D;
 #pragma unroll
   for (int t = 0; t < D / 64; ++t) {
-    ok[lane + 64 * t] += a.scale * dk[t];
-    ov[lane + 64 * t] += dv[t];
+    ok[lane + 64 * t] += float(double(a.scale) * dk[t]);
+    ov[lane + 64 * t] += float(dv[t]);
   }
 }
 

@@ -8,6 +8,7 @@
 // One thread owns 4 consecutive head_dim elements of one (row, head); the
 // n partial pointers travel in the kernel arguments.
 #include <algorithm>
+#include <type_traits>
 
 #include "kernels.hpp"
 
@@ -66,21 +67,23 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 }
 
 // delta[b, h, i] = sum_d dO[b, i, h, d] * O[b, i, h, d]; 8 elements per
-// lane, head_dim / 8 lanes per row (a power of two <= 16).
+// lane, head_dim / 8 lanes per row (a power of two <= 16).  fp32 inputs (the
+// exact path) sum in fp64, bf16 inputs in fp32.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void delta_kernel(const T* o, const T* d_o, float* delta,
                                                     int64_t rows, int64_t len_q, int32_t heads) {
+  using Acc = std::conditional_t<sizeof(T) == 2, float, double>;
   constexpr int LPR = D / 8;
   const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
   const int64_t rh = t / LPR;
   const int c = int(t % LPR);
-  float s = 0.f;
+  Acc s = 0;
   if (rh < rows) {
     const T* po = o + rh * D + 8 * c;
     const T* pd = d_o + rh * D + 8 * c;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float x, y;
+      Acc x, y;
       if constexpr (sizeof(T) == 2) {
         x = bf16_to_f32(po[e]);
         y = bf16_to_f32(pd[e]);
@@ -96,7 +99,7 @@ __global__ __launch_bounds__(256) void delta_kernel(const T* o, const T* d_o, fl
   if (rh < rows && c == 0) {
     const int h = int(rh % heads);
     const int64_t bi = rh / heads;
-    delta[((bi / len_q) * heads + h) * len_q + bi % len_q] = s;
+    delta[((bi / len_q) * heads + h) * len_q + bi % len_q] = float(s);
   }
 }
 

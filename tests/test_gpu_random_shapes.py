@@ -1,0 +1,77 @@
+"""Seeded random chunk pairs against the float64 oracle: head grouping 1..8,
+head_dim 64 and 128, batch 1 or 2, query and key lengths from 1 to 400 with
+arbitrary global offsets (so tiles are ragged and the causal edge or the
+window band falls anywhere), causal or not, with and without a sliding
+window, bf16 and fp32.  Forward (O, LSE) and backward (dQ, dK, dV from the
+oracle's final O and LSE) of every pair."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_context_exact_amd import dfa as D
+from long_context_exact_amd.synth import bf16_round
+
+from _util import DEV, check_grad, check_lse, check_o, rand, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu(dfa_lib):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _draw(n, seed=2024):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        hkv = int(rng.choice([1, 2, 4]))
+        group = int(rng.choice([1, 2, 4, 8]))
+        dh = int(rng.choice([64, 128]))
+        b = int(rng.choice([1, 2]))
+        lq, lk = (int(x) for x in rng.integers(1, 401, size=2))
+        q0 = int(rng.integers(0, 601))
+        k0 = max(0, q0 + int(rng.integers(-500, 101)))  # mostly keys at or before the queries
+        causal = bool(rng.random() < 0.8)
+        window = int(rng.integers(1, 301)) if causal and rng.random() < 0.4 else 0
+        dtype = "f32" if rng.random() < 0.25 else "bf16"
+        cases.append((i, b, lq, lk, q0, k0, hkv * group, hkv, dh, causal, window, dtype))
+    return cases
+
+
+@pytest.mark.parametrize("case", _draw(48), ids=lambda c: f"r{c[0]}")
+def test_random_pair(case):
+    i, b, lq, lk, q0, k0, hq, hkv, dh, causal, win, dt = case
+    print(f"case random pair {case}", flush=True)
+    rng = np.random.default_rng(1000 + i)
+    scale = dh ** -0.5
+    q = rand(rng, (b, lq, hq, dh), dt)
+    k = rand(rng, (b, lk, hkv, dh), dt)
+    v = rand(rng, (b, lk, hkv, dh), dt)
+    d_o = rand(rng, (b, lq, hq, dh), dt)
+    desc = D.make_desc(b, hq, hkv, dh, lq, lk, q0, k0, causal, scale, dt, window=win)
+    qd, kd, vd = to_dev(q, dt), to_dev(k, dt), to_dev(v, dt)
+    o = torch.full((b, lq, hq, dh), 7.0, device=DEV)
+    lse = torch.full((b, hq, lq), 7.0, device=DEV)
+    D.dfa_attn_fwd_partial(desc, qd, kd, vd, o, lse)
+    ro, rl = oracle.attention_fwd(q, k, v, scale, causal, q0, k0, window=win)
+    check_o(to_np(o), ro, dt)
+    check_lse(to_np(lse), rl, dt)
+
+    o_in = to_dev(ro.astype(np.float32) if dt == "f32" else bf16_round(ro.astype(np.float32)), dt)
+    lse_in = torch.from_numpy(rl.astype(np.float32)).to(DEV)
+    delta = torch.empty_like(lse_in)
+    dq = torch.zeros(b, lq, hq, dh, device=DEV)
+    dk = torch.zeros(b, lk, hkv, dh, device=DEV)
+    dv = torch.zeros(b, lk, hkv, dh, device=DEV)
+    D.dfa_attn_bwd(desc, qd, kd, vd, o_in, lse_in, to_dev(d_o, dt), delta, True, dq, dk, dv)
+    rq, rk, rv = oracle.attention_bwd(q, k, v, to_np(o_in), rl, d_o, scale, causal, q0, k0,
+                                      window=win)
+    for g, r, n in ((dq, rq, "dQ"), (dk, rk, "dK"), (dv, rv, "dV")):
+        if np.linalg.norm(r) == 0:
+            assert np.all(to_np(g) == 0), n
+        else:
+            check_grad(to_np(g), r, dt, n)
