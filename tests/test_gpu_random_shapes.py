@@ -1,9 +1,13 @@
-"""Seeded random chunk pairs against the float64 oracle: head grouping 1..8,
+"""Seeded random chunk pairs and whole sequences against the float64 oracle.
+
+Pairs: head grouping 1..8,
 head_dim 64 and 128, batch 1 or 2, query and key lengths from 1 to 400 with
 arbitrary global offsets (so tiles are ragged and the causal edge or the
 window band falls anywhere), causal or not, with and without a sliding
 window, bf16 and fp32.  Forward (O, LSE) and backward (dQ, dK, dV from the
-oracle's final O and LSE) of every pair."""
+oracle's final O and LSE) of every pair.  Sequences: 1 to 6 workers of 1 to 160
+tokens through the runner (balanced or unbalanced schedule, sliding window,
+global tokens), every partial, the merge and the backward."""
 
 import numpy as np
 import pytest
@@ -75,3 +79,55 @@ def test_random_pair(case):
             assert np.all(to_np(g) == 0), n
         else:
             check_grad(to_np(g), r, dt, n)
+
+
+def _draw_sequences(n, seed=2025):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        p = int(rng.integers(1, 7))
+        c = int(rng.integers(1, 161))
+        hkv = int(rng.choice([1, 2]))
+        hq = hkv * int(rng.choice([1, 2, 4, 8]))
+        dh = int(rng.choice([64, 128]))
+        b = int(rng.choice([1, 2]))
+        dt = "f32" if rng.random() < 0.25 else "bf16"
+        kind = rng.random()
+        win = g = 0
+        balanced = True
+        if kind < 0.3:
+            win = int(rng.integers(1, p * c + 2))
+        elif kind < 0.5:
+            win = int(rng.integers(1, p * c + 2))
+            g = int(rng.integers(1, c + 1))
+        elif kind < 0.6:
+            balanced = False
+        cases.append((i, p, c, b, hq, hkv, dh, dt, win, g, balanced))
+    return cases
+
+
+@pytest.mark.parametrize("case", _draw_sequences(24), ids=lambda c: f"s{c[0]}")
+def test_random_sequence(case):
+    """Whole sequences through the runner (schedule, every partial, the
+    merge, the backward) against the oracle's whole-sequence attention."""
+    from long_context_exact_amd.runner import ChunkedCausalAttention
+    from _util import run_sequence
+    i, p, c, b, hq, hkv, dh, dt, win, g, balanced = case
+    print(f"case random sequence {case}", flush=True)
+    rng = np.random.default_rng(2000 + i)
+    q = [rand(rng, (b, c, hq, dh), dt) for _ in range(p)]
+    k = [rand(rng, (b, c, hkv, dh), dt) for _ in range(p)]
+    v = [rand(rng, (b, c, hkv, dh), dt) for _ in range(p)]
+    d_o = [rand(rng, (b, c, hq, dh), dt) for _ in range(p)]
+    att = ChunkedCausalAttention(p, c, b, hq, hkv, dh, dt, balanced=balanced, window=win,
+                                 n_global=g)
+    got = run_sequence(att, q, k, v, d_o)
+    qf, kf, vf, dof = (np.concatenate(x, axis=1).astype(np.float64) for x in (q, k, v, d_o))
+    ro, rl = oracle.attention_fwd(qf, kf, vf, att.scale, True, 0, 0, window=win, n_global=g)
+    check_o(np.concatenate(got["o"], 1), ro, dt, stored_bf16=dt == "bf16")
+    check_lse(np.concatenate(got["lse"], 2), rl, dt)
+    rq, rk, rv = oracle.attention_bwd(qf, kf, vf, ro, rl, dof, att.scale, True, 0, 0,
+                                      window=win, n_global=g)
+    check_grad(np.concatenate(got["dq"], 1), rq, dt, "dQ")
+    check_grad(np.concatenate(got["dk"], 1), rk, dt, "dK")
+    check_grad(np.concatenate(got["dv"], 1), rv, dt, "dV")
