@@ -46,6 +46,18 @@ def _draw(n, seed=2024):
     return cases
 
 
+def _check_grad_or_zero(g, r, dt, n):
+    """A gradient that is exactly zero in exact arithmetic (every row sees at
+    most one key: P = 1, O = V, dS = P (dP - D) = 0) comes out of the kernels
+    at fp32 rounding level (a few 1e-7), not bitwise zero: the bound there is
+    the absolute 1e-5 of the exact path; anything else takes the usual check."""
+    if np.linalg.norm(r) == 0:
+        err = float(np.max(np.abs(g))) if g.size else 0.0
+        assert err <= 1e-5, f"{n}: exact zero, got max |g| {err}"
+    else:
+        check_grad(g, r, dt, n)
+
+
 @pytest.mark.parametrize("case", _draw(48), ids=lambda c: f"r{c[0]}")
 def test_random_pair(case):
     i, b, lq, lk, q0, k0, hq, hkv, dh, causal, win, dt = case
@@ -75,10 +87,7 @@ def test_random_pair(case):
     rq, rk, rv = oracle.attention_bwd(q, k, v, to_np(o_in), rl, d_o, scale, causal, q0, k0,
                                       window=win)
     for g, r, n in ((dq, rq, "dQ"), (dk, rk, "dK"), (dv, rv, "dV")):
-        if np.linalg.norm(r) == 0:
-            assert np.all(to_np(g) == 0), n
-        else:
-            check_grad(to_np(g), r, dt, n)
+        _check_grad_or_zero(to_np(g), r, dt, n)
 
 
 def _draw_sequences(n, seed=2025):
