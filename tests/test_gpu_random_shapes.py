@@ -58,7 +58,28 @@ def _check_grad_or_zero(g, r, dt, n):
         check_grad(g, r, dt, n)
 
 
-@pytest.mark.parametrize("case", _draw(48), ids=lambda c: f"r{c[0]}")
+def _draw_long(n, seed=79):
+    """Long query chunks against short key chunks: few key blocks with many
+    rows each, the shape for which dK/dV splits a block's rows over several
+    workgroups."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        hkv = int(rng.choice([1, 2, 4]))
+        group = int(rng.choice([1, 2, 4, 8]))
+        dh = int(rng.choice([64, 128]))
+        b = int(rng.choice([1, 2]))
+        lq, lk = int(rng.integers(1024, 4097)), int(rng.integers(1, 701))
+        q0 = int(rng.integers(0, 3000))
+        k0 = max(0, q0 + int(rng.integers(-2000, 50)))
+        causal = bool(rng.random() < 0.85)
+        window = int(rng.integers(1, 1500)) if causal and rng.random() < 0.4 else 0
+        dtype = "f32" if rng.random() < 0.15 else "bf16"
+        cases.append((100 + i, b, lq, lk, q0, k0, hkv * group, hkv, dh, causal, window, dtype))
+    return cases
+
+
+@pytest.mark.parametrize("case", _draw(48) + _draw_long(8), ids=lambda c: f"r{c[0]}")
 def test_random_pair(case):
     i, b, lq, lk, q0, k0, hq, hkv, dh, causal, win, dt = case
     print(f"case random pair {case}", flush=True)
