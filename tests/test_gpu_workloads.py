@@ -44,7 +44,7 @@ def _inputs(w, q_chunks, kv_chunks):
     return host
 
 
-def _run(w, att, host, owners, items, backward):
+def _run(w, att, host, owners, items, backward, kv_bufs=None):
     td = TD[w.dtype]
     dev = {t: {c: torch.from_numpy(x).to(DEV).to(td) for c, x in host[t].items()} for t in host}
     q, k, v, d_o = dev[0], dev[1], dev[2], dev[3]
@@ -56,7 +56,7 @@ def _run(w, att, host, owners, items, backward):
         att.merge_owner(a, partials, o[a], lse[a])
     res = {"o": o, "lse": lse, "partials": partials}
     if backward:
-        kvs = sorted({it[3] for it in items})
+        kvs = kv_bufs if kv_bufs is not None else sorted({it[3] for it in items})
         dq = {a: torch.zeros(att.q_shape(), device=DEV) for a in owners}
         dk = {c: torch.zeros(att.kv_shape(), device=DEV) for c in kvs}
         dv = {c: torch.zeros(att.kv_shape(), device=DEV) for c in kvs}
@@ -224,3 +224,52 @@ def test_windowed_worker_share_forward_backward():
     assert rel_fro(go, wo) <= 2e-2
     assert rel_fro(np.concatenate(got_dq), np.concatenate(want_dq)) <= 2e-2
     _check_grad_identities(w, host, res, [a], kvs)
+
+
+def test_global_window_worker_share_forward_backward():
+    """Worker 15's share with a 4096-token window and the first 1024 tokens
+    global (App. F, replicated): its global item (the 1024 global keys, read
+    from chunk 0) and its window pairs (15, 14), (15, 15); sampled rows of the
+    merged O / LSE and of dQ against the oracle's plain definition over the
+    whole prefix, and the dK / dV identities over chunk 0 and the two window
+    chunks.  Chunks 1..13 hold neither global tokens nor keys inside these
+    rows' windows: they enter the oracle as zeros, which its mask drops."""
+    w = WORKLOADS["gqa64x8_512k_win4k_g1k_w15"]
+    print(f"case {w.name}", flush=True)
+    att = ChunkedCausalAttention(w.workers, w.chunk, w.batch, w.heads_q, w.heads_kv, w.head_dim,
+                                 w.dtype, window=w.window, n_global=w.n_global)
+    a, c, win, g = w.share_of, w.chunk, w.window, w.n_global
+    items = att.items_of_owner(a)
+    assert sorted(it[3] for it in items) == [-1, a - 1, a]
+    kvs = [0, a - 1, a]
+    host = _inputs(w, [a], kvs)
+    res = _run(w, att, host, [a], items, True, kv_bufs=kvs)
+    grp = w.heads_q // w.heads_kv
+    zeros = np.zeros((w.batch, c, 1, w.head_dim))
+    got_o, want_o, got_dq, want_dq = [], [], [], []
+    for h in (0, w.heads_q - 1):
+        hk = h // grp
+        kp = np.concatenate([host[1][j][:, :, hk:hk + 1].astype(np.float64) if j in kvs else zeros
+                             for j in range(a + 1)], 1)
+        vp = np.concatenate([host[2][j][:, :, hk:hk + 1].astype(np.float64) if j in kvs else zeros
+                             for j in range(a + 1)], 1)
+        for r in (0, 1, win - 1, win, c // 2, c - 1):
+            qr = host[0][a][:, r:r + 1, h:h + 1].astype(np.float64)
+            ro, rl = oracle.attention_fwd(qr, kp, vp, w.scale, True, a * c + r, 0, window=win,
+                                          n_global=g)
+            got_o.append(to_np(res["o"][a][:, r, h]).ravel())
+            want_o.append(ro.ravel())
+            check_lse(to_np(res["lse"][a][:, h, r]).reshape(rl.shape), rl, "bf16",
+                      f"LSE row {r} head {h}")
+            dor = host[3][a][:, r:r + 1, h:h + 1].astype(np.float64)
+            rq = oracle.attention_bwd(qr, kp, vp, ro, rl, dor, w.scale, True, a * c + r, 0,
+                                      window=win, n_global=g)[0]
+            got_dq.append(to_np(res["dq"][a][:, r, h]).ravel())
+            want_dq.append(rq.ravel())
+    go, wo = np.concatenate(got_o), np.concatenate(want_o)
+    assert np.max(np.abs(go - wo)) <= 1e-2
+    assert rel_fro(go, wo) <= 2e-2
+    assert rel_fro(np.concatenate(got_dq), np.concatenate(want_dq)) <= 2e-2
+    _check_grad_identities(w, host, res, [a], kvs)
+    # keys of chunk 0 past the global prefix are seen by no row of this share
+    assert torch.all(res["dv"][0][:, g:] == 0) and torch.all(res["dk"][0][:, g:] == 0)
