@@ -52,6 +52,9 @@ typedef enum {
   DFA_ERR_HIP = 4           /* the HIP runtime reported an error            */
 } dfa_status;
 
+/* Element type of Q, K, V, dO and the final O.  DFA_BF16: bf16 matrix-core
+ * products with fp32 accumulation.  DFA_F32: the exact path; fp32 in and
+ * out, scores, exponentials and sums carried in fp64. */
 typedef enum { DFA_F32 = 0, DFA_BF16 = 1 } dfa_dtype;
 
 /* One chunk pair of a schedule.  kind: 0 = diagonal pair (q_chunk ==
@@ -67,7 +70,7 @@ typedef struct {
 
 /* Shape and masking of one (query chunk, key/value chunk) pair. */
 typedef struct {
-  int32_t batch;        /* >= 1                                            */
+  int32_t batch;        /* 0 .. 65535 (0: nothing to do)                  */
   int32_t heads_q;      /* >= 1, a multiple of heads_kv; heads_q *       */
                         /* head_dim < 2^21 (else DFA_ERR_UNSUPPORTED)     */
   int32_t heads_kv;     /* >= 1                                            */
