@@ -150,11 +150,11 @@ dfa_status dfa_global_window_schedule(int32_t num_workers, int64_t chunk_len,
  *   after a query tile's last row are skipped (§2, §3.2), and with a
  *   window so are key tiles entirely outside every window of the tile's
  *   rows (App. F).  For bf16 inputs the call first writes a transposed copy
- *   of v into a scratch buffer the library allocates once per device (grown
- *   on demand, kept until the process ends; growing it synchronizes the
- *   device).  Every call that uses that buffer (this one, and dfa_attn_bwd
- *   when it splits rows) must be ordered against the others on one device:
- *   issue them on one stream. */
+ *   of v into a scratch buffer the library owns, one per device and stream
+ *   (allocated on first use, grown on demand after the stream's earlier work
+ *   has finished, kept until the process ends): calls on one stream are
+ *   ordered, and calls on different streams use different buffers and may
+ *   run concurrently. */
 dfa_status dfa_attn_fwd_partial(const dfa_attn_desc* desc, const void* q,
                                 const void* k, const void* v, float* o_part,
                                 float* lse, void* hip_stream);
@@ -193,11 +193,9 @@ dfa_status dfa_lse_merge(int32_t n, const float* const* o_parts,
  * to their owners).  Each call is deterministic.  When few key blocks carry
  * most of the pair's rows (a short key range against a long query chunk, a
  * window band) the dK/dV part splits each block's rows over several
- * workgroups and sums their partials in a fixed order, in a scratch buffer
- * the library allocates once per device (grown on demand, kept until the
- * process ends; growing it synchronizes the device), the same buffer
- * dfa_attn_fwd_partial uses: on one device such calls must not run
- * concurrently (issue them on one stream); calls on one stream are ordered. */
+ * workgroups and sums their partials in a fixed order, in the library's
+ * scratch buffer of the call's stream (the one dfa_attn_fwd_partial uses:
+ * one per device and stream, so calls on different streams may overlap). */
 dfa_status dfa_attn_bwd(const dfa_attn_desc* desc, const void* q,
                         const void* k, const void* v, const void* o,
                         const float* lse, const void* d_o, float* delta,

@@ -358,7 +358,7 @@ dfa_status launch_dkdv(const dfa_attn_desc& d, BwdArgs a, hipStream_t s) {
     const size_t per = size_t(2) * d.batch * d.len_kv * d.heads_kv * D * sizeof(float);
     split = std::min<int64_t>(split, int64_t(kMaxSplitBytes / per));
     if (split > 1) {
-      a.ws = static_cast<float*>(device_workspace(size_t(split) * per));
+      a.ws = static_cast<float*>(device_workspace(size_t(split) * per, s));
       if (a.ws != nullptr) a.rsplit = int32_t(split);
     }
   }

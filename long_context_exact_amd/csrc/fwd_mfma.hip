@@ -368,7 +368,7 @@ dfa_status launch_fwd(const dfa_attn_desc& d, const void* q, const void* k, cons
     return fail(DFA_ERR_UNSUPPORTED, "dfa_attn_fwd_partial: len_kv too large for 32-bit V^T offsets");
   if (a.vt_ld > 0) {
     const size_t bytes = size_t(d.batch) * d.heads_kv * d.head_dim * size_t(a.vt_ld) * 2;
-    uint16_t* vt = static_cast<uint16_t*>(device_workspace(bytes));
+    uint16_t* vt = static_cast<uint16_t*>(device_workspace(bytes, s));
     if (vt == nullptr)
       return fail(DFA_ERR_HIP, "dfa_attn_fwd_partial: cannot allocate " + std::to_string(bytes) +
                                    " bytes of V^T scratch");

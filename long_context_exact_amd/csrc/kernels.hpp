@@ -52,10 +52,11 @@ inline bool pair_is_full(const dfa_attn_desc& d, int64_t tile) {
   return all_visible && in_window && d.len_kv % tile == 0;
 }
 
-// Library-owned device scratch of at least `bytes` (one buffer per device,
-// shared by every call on it: calls that use it must be stream-ordered);
-// nullptr if it cannot be allocated.
-void* device_workspace(size_t bytes);
+// Library-owned device scratch of at least `bytes` for work enqueued on
+// `stream` (one buffer per device and stream: the calls on a stream are
+// ordered, calls on different streams use different buffers); nullptr if it
+// cannot be allocated.
+void* device_workspace(size_t bytes, hipStream_t stream);
 
 // X [B][len][H][d] bf16 -> X^T [B][H][d][ld] (ld a multiple of 64, >= len):
 // keys permuted within 16-key groups (index bits 2 and 3 swapped), keys past

@@ -1,32 +1,40 @@
-// Library-owned device scratch, one buffer per device, grown on demand and
-// kept until the process ends.  Kernels of one call use it in stream order;
-// calls that use it must therefore be ordered on one device (one stream).
+// Library-owned device scratch: one buffer per (device, stream), grown on
+// demand and kept until the process ends.  The kernels of one call use it in
+// stream order, and calls on one stream are ordered, so a stream's buffer is
+// never in use by two calls at once; calls on different streams get
+// different buffers and may overlap.
+#include <map>
 #include <mutex>
+#include <utility>
 
 #include "kernels.hpp"
 
 namespace dfa {
 
-void* device_workspace(size_t bytes) {
+void* device_workspace(size_t bytes, hipStream_t stream) {
+  struct Buf {
+    void* ptr = nullptr;
+    size_t cap = 0;
+  };
   static std::mutex mu;
-  static void* ptr[64] = {};
-  static size_t cap[64] = {};
+  static std::map<std::pair<int, hipStream_t>, Buf> bufs;
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
   std::lock_guard<std::mutex> lock(mu);
-  if (cap[dev] >= bytes) return ptr[dev];
-  if (ptr[dev] != nullptr) {  // work queued with the old buffer must finish first
-    if (hipDeviceSynchronize() != hipSuccess || hipFree(ptr[dev]) != hipSuccess) return nullptr;
-    ptr[dev] = nullptr;
-    cap[dev] = 0;
+  Buf& b = bufs[{dev, stream}];
+  if (b.cap >= bytes) return b.ptr;
+  if (b.ptr != nullptr) {  // work queued on this stream with the old buffer must finish first
+    if (hipStreamSynchronize(stream) != hipSuccess || hipFree(b.ptr) != hipSuccess) return nullptr;
+    b.ptr = nullptr;
+    b.cap = 0;
   }
   void* p = nullptr;
   if (hipMalloc(&p, bytes) != hipSuccess) {
     (void)hipGetLastError();
     return nullptr;
   }
-  ptr[dev] = p;
-  cap[dev] = bytes;
+  b.ptr = p;
+  b.cap = bytes;
   return p;
 }
 
