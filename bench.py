@@ -200,6 +200,35 @@ def copy_calibration(gib: float):
     print(json.dumps({"copy_bytes_per_launch": n, "launches": 3}), flush=True)
 
 
+def mfma_ceiling(seconds: float):
+    """The dense bf16 matrix-core rate this board sustains: the library's
+    calibration loop (register operands, no memory traffic) run for
+    `seconds` with constant and with switching random operands, two
+    workgroups of four waves per CU (two waves per SIMD, like the kernels)."""
+    import torch
+    from long_context_exact_amd import dfa as D
+    wg = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros(wg * 256, device="cuda")
+    iters = 1 << 16
+    out = {}
+    # mode bit 0: random operands; bit 1: accumulators held in the AGPR file
+    for name, rnd in (("constant_operands", 0), ("random_operands", 1),
+                      ("constant_operands_agpr_acc", 2), ("random_operands_agpr_acc", 3)):
+        D.dfa_test_mfma_loop(wg, 256, rnd, sink)
+        torch.cuda.synchronize()
+        t0, n = time.time(), 0  # wall clock, to line up with an outside power monitor
+        while time.time() - t0 < seconds:
+            D.dfa_test_mfma_loop(wg, iters, rnd, sink)
+            torch.cuda.synchronize()
+            n += 1
+        dt = time.time() - t0
+        out[name] = {"tflops": round((1 << 19) * wg * iters * n / dt / 1e12, 1), "seconds": round(dt, 2),
+                     "launches": n}
+        print(json.dumps({"phase": name, "t0": t0, "t1": t0 + dt}), flush=True)
+    print(json.dumps({"metric": "sustained dense bf16 MFMA TFLOP/s (calibration loop)",
+                      "workgroups": wg, "published_peak": PEAK_TFLOPS["bf16"], **out}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -211,7 +240,13 @@ def main():
     ap.add_argument("--copy-gib", type=float, default=0.0,
                     help="only copy this many GiB device-to-device 3 times (the reference kernel "
                          "whose counter readings calibrate FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--mfma-ceiling", type=float, default=0.0,
+                    help="only run the matrix-core calibration loop for this many seconds per "
+                         "operand kind and print the sustained dense bf16 rate")
     args = ap.parse_args()
+    if args.mfma_ceiling > 0:
+        mfma_ceiling(args.mfma_ceiling)
+        return
     if args.copy_gib > 0:
         copy_calibration(args.copy_gib)
         return

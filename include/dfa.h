@@ -234,6 +234,21 @@ dfa_status dfa_test_bwd_part(const dfa_attn_desc* desc, const void* q,
                              float* dk, float* dv, int32_t part,
                              void* hip_stream);
 
+/* Matrix-core calibration: `workgroups` workgroups of 4 waves, every wave
+ * running 4 independent chains of iters bf16 32x32x16 matrix products
+ * (v_mfma_f32_32x32x16_bf16, 32768 FLOP each: 2^19 * workgroups * iters FLOP
+ * per call) on register operands, with no memory traffic.  mode bit 0 set:
+ * pseudo-random operand bits that keep switching, as real data does; clear:
+ * one constant operand pair.  mode bit 1 set: the accumulators live in the
+ * accumulation registers (AGPRs); clear: wherever the compiler puts them.
+ * Other bits must be 0.  Timed over several seconds it gives the dense bf16
+ * rate the board sustains under its power and current limits.
+ * sink: DEVICE buffer of >= workgroups * 256 floats (practically never
+ * written).  iters even, >= 2; workgroups in [1, 65536]. */
+dfa_status dfa_test_mfma_loop(int32_t workgroups, int32_t iters,
+                              int32_t mode, float* sink,
+                              void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -195,6 +195,22 @@ extern "C" dfa_status dfa_test_bwd_part(const dfa_attn_desc* desc, const void* q
   }
 }
 
+extern "C" dfa_status dfa_test_mfma_loop(int32_t workgroups, int32_t iters,
+                                         int32_t mode, float* sink,
+                                         void* hip_stream) {
+  try {
+    if (workgroups < 1 || workgroups > 65536 || iters < 2 || iters % 2 != 0)
+      return fail(DFA_ERR_INVALID,
+                  "dfa_test_mfma_loop: workgroups in [1, 65536], iters even and >= 2");
+    if (mode < 0 || mode > 3) return fail(DFA_ERR_INVALID, "dfa_test_mfma_loop: mode in [0, 3]");
+    if (sink == nullptr) return fail(DFA_ERR_INVALID, "dfa_test_mfma_loop: sink is null");
+    return launch_mfma_loop(workgroups, iters, mode, sink,
+                            static_cast<hipStream_t>(hip_stream));
+  } catch (...) {
+    return fail(DFA_ERR_INVALID, "dfa_test_mfma_loop: internal error");
+  }
+}
+
 extern "C" int32_t dfa_version(void) { return 100; }
 
 extern "C" dfa_status dfa_test_tile_shape(const dfa_attn_desc* desc, int32_t* bm, int32_t* bn) {

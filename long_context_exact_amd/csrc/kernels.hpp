@@ -64,6 +64,12 @@ void* device_workspace(size_t bytes, hipStream_t stream);
 dfa_status launch_kv_transpose(const uint16_t* x, uint16_t* xt, int32_t batch, int64_t len,
                                int32_t heads, int32_t head_dim, int64_t ld, hipStream_t s);
 
+// Matrix-core calibration loop (test support): `workgroups` workgroups of
+// 4 waves, each wave 4 chains of `iters` / 2 x 2 bf16 32x32x16 products;
+// sink holds >= workgroups * 256 floats.
+dfa_status launch_mfma_loop(int32_t workgroups, int32_t iters, int32_t mode, float* sink,
+                            hipStream_t s);
+
 // o = 0, lse = -inf for every row (a chunk pair with no keys).
 dfa_status launch_fill_empty(int64_t n_o, float* o, int64_t n_lse, float* lse,
                              hipStream_t s);

@@ -30,7 +30,7 @@ EXPORTED = (
     "dfa_balanced_schedule", "dfa_window_schedule", "dfa_global_window_schedule",
     "dfa_attn_fwd_partial", "dfa_lse_merge", "dfa_attn_bwd",
     "dfa_last_error", "dfa_version", "dfa_test_tile_shape", "dfa_test_fwd_tile_visits",
-    "dfa_test_bwd_part",
+    "dfa_test_bwd_part", "dfa_test_mfma_loop",
 )
 
 
@@ -92,10 +92,11 @@ def lib() -> ctypes.CDLL:
         L.dfa_test_fwd_tile_visits.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P]
         L.dfa_test_bwd_part.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, P, P, I32,
                                         P]
+        L.dfa_test_mfma_loop.argtypes = [I32, I32, I32, P, P]
         for name in ("dfa_balanced_schedule", "dfa_window_schedule", "dfa_global_window_schedule",
                      "dfa_attn_fwd_partial", "dfa_lse_merge",
                      "dfa_attn_bwd", "dfa_test_tile_shape", "dfa_test_fwd_tile_visits",
-                     "dfa_test_bwd_part"):
+                     "dfa_test_bwd_part", "dfa_test_mfma_loop"):
             getattr(L, name).restype = I32
         L.dfa_last_error.argtypes = []
         L.dfa_last_error.restype = ctypes.c_char_p
@@ -264,3 +265,14 @@ def dfa_test_bwd_part(desc: AttnDesc, q, k, v, lse, d_o, delta, dq, dk, dv, part
             _ptr(dk, "dk", ks, f32) if part == 1 else None,
             _ptr(dv, "dv", ks, f32) if part == 1 else None)
     _check(lib().dfa_test_bwd_part(ctypes.byref(desc), *args, int(part), _stream(stream)))
+
+
+def dfa_test_mfma_loop(workgroups: int, iters: int, mode: int, sink, stream=None):
+    """Matrix-core calibration loop (2^19 * workgroups * iters bf16 FLOP);
+    mode bit 0: random operands, bit 1: accumulators in AGPRs."""
+    if not isinstance(sink, torch.Tensor) or sink.dtype != torch.float32 or \
+            sink.numel() < workgroups * 256:
+        raise ValueError("sink must be a float32 tensor of at least workgroups * 256 elements")
+    _check(lib().dfa_test_mfma_loop(int(workgroups), int(iters), int(mode),
+                                    _ptr(sink, "sink", tuple(sink.shape), torch.float32),
+                                    _stream(stream)))

@@ -234,3 +234,12 @@ def test_binding_rejects_mismatched_tensors(dfa_lib):
     cpu = torch.zeros(1, 16, 2, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="HIP device"):
         dfa_lib.dfa_attn_fwd_partial(d, cpu, cpu, cpu, None, None)
+
+
+def test_mfma_loop_argument_errors(dfa_lib):
+    L = dfa_lib.lib()
+    assert L.dfa_test_mfma_loop(0, 2, 0, FAKE, None) == D.DFA_ERR_INVALID      # no workgroups
+    assert L.dfa_test_mfma_loop(4, 3, 0, FAKE, None) == D.DFA_ERR_INVALID      # odd iters
+    assert L.dfa_test_mfma_loop(4, 2, 1, None, None) == D.DFA_ERR_INVALID      # no sink
+    assert L.dfa_test_mfma_loop(4, 2, 4, FAKE, None) == D.DFA_ERR_INVALID      # unknown mode
+    assert dfa_lib.dfa_last_error().startswith("dfa_test_mfma_loop")

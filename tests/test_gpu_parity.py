@@ -282,3 +282,14 @@ def test_backward_accumulates_into_existing_gradients():
     check_grad(to_np(dk) - 2, rk, "bf16", "dK")
     check_grad(to_np(dv) - 3, rv, "bf16", "dV")
     check_lse(to_np(delta), oracle.attention_delta(to_np(o_in), d_o), "f32", "delta")
+
+
+def test_mfma_calibration_loop_runs():
+    """The matrix-core calibration loop runs in all four modes (constant or
+    random operands, accumulators anywhere or in AGPRs) and leaves its sink
+    untouched."""
+    sink = torch.zeros(8 * 256, device=DEV)
+    for mode in range(4):
+        D.dfa_test_mfma_loop(8, 64, mode, sink)
+    torch.cuda.synchronize()
+    assert torch.all(sink == 0)
