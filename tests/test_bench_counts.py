@@ -49,3 +49,16 @@ def test_global_visible_pairs_sum_to_the_masked_pairs(p, chunk, window, g):
         if it[3] == -1:  # the global item: every causal key of the prefix
             assert bench.visible_pairs(it, chunk, window, g) == sum(
                 min(g, it[2] * chunk + i + 1) for i in range(chunk))
+
+
+def test_traffic_summary_matches_the_kernel_sources():
+    """The committed HBM-traffic summary was taken on the current sources of
+    every kernel it covers, and is withheld for any other workload."""
+    import json
+    doc = json.load(open(bench.TRAFFIC_FILE))
+    for name in bench.KERNEL_SOURCES:
+        assert doc["kernels"][name]["source_digest"] == bench.source_digest(name), name
+        t = bench.traffic_of(name, 1, doc["workload"])
+        # each figure is a mean over launches, rounded to whole bytes on its own
+        assert t is not None and abs(t["bytes_per_launch"] - t["fetch"] - t["write"]) <= 2, name
+        assert bench.traffic_of(name, 1, doc["workload"] + "_other") is None
