@@ -189,44 +189,19 @@ def cpu_baseline(w, host, worker, budget_s, kv_lo):
             "fwd_gflops": round(fw[1] / fw[0] / 1e9, 2), "bwd_gflops": round(bw[1] / bw[0] / 1e9, 2)}
 
 
-def copy_calibration(gib: float):
+# Bytes of the device-to-device copy every run makes before timing: a plain
+# copy kernel of known size, whose FETCH_SIZE / WRITE_SIZE readings in the same
+# profiling run scale the attention kernels' readings to bytes.
+REFERENCE_COPY_BYTES = 1 << 30
+
+
+def reference_copy():
     import torch
-    n = int(gib * (1 << 30))
-    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    src = torch.ones(REFERENCE_COPY_BYTES, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
+    dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes_per_launch": n, "launches": 3}), flush=True)
-
-
-def mfma_ceiling(seconds: float):
-    """The dense bf16 matrix-core rate this board sustains: the library's
-    calibration loop (register operands, no memory traffic) run for
-    `seconds` with constant and with switching random operands, two
-    workgroups of four waves per CU (two waves per SIMD, like the kernels)."""
-    import torch
-    from long_context_exact_amd import dfa as D
-    wg = 2 * torch.cuda.get_device_properties(0).multi_processor_count
-    sink = torch.zeros(wg * 256, device="cuda")
-    iters = 1 << 16
-    out = {}
-    # mode bit 0: random operands; bit 1: accumulators held in the AGPR file
-    for name, rnd in (("constant_operands", 0), ("random_operands", 1),
-                      ("constant_operands_agpr_acc", 2), ("random_operands_agpr_acc", 3)):
-        D.dfa_test_mfma_loop(wg, 256, rnd, sink)
-        torch.cuda.synchronize()
-        t0, n = time.time(), 0  # wall clock, to line up with an outside power monitor
-        while time.time() - t0 < seconds:
-            D.dfa_test_mfma_loop(wg, iters, rnd, sink)
-            torch.cuda.synchronize()
-            n += 1
-        dt = time.time() - t0
-        out[name] = {"tflops": round((1 << 19) * wg * iters * n / dt / 1e12, 1), "seconds": round(dt, 2),
-                     "launches": n}
-        print(json.dumps({"phase": name, "t0": t0, "t1": t0 + dt}), flush=True)
-    print(json.dumps({"metric": "sustained dense bf16 MFMA TFLOP/s (calibration loop)",
-                      "workgroups": wg, "published_peak": PEAK_TFLOPS["bf16"], **out}), flush=True)
+    del src, dst
 
 
 def main():
@@ -237,19 +212,7 @@ def main():
     ap.add_argument("--workload", default="gqa64x8_512k_w15")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--copy-gib", type=float, default=0.0,
-                    help="only copy this many GiB device-to-device 3 times (the reference kernel "
-                         "whose counter readings calibrate FETCH_SIZE / WRITE_SIZE)")
-    ap.add_argument("--mfma-ceiling", type=float, default=0.0,
-                    help="only run the matrix-core calibration loop for this many seconds per "
-                         "operand kind and print the sustained dense bf16 rate")
     args = ap.parse_args()
-    if args.mfma_ceiling > 0:
-        mfma_ceiling(args.mfma_ceiling)
-        return
-    if args.copy_gib > 0:
-        copy_calibration(args.copy_gib)
-        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (the schedule's "
               "workers are emulated as work items on one device); run with --gpus 1.",
@@ -278,6 +241,7 @@ def main():
         merged = {a: att.items_of_owner(a) for a in owners}
     kv_needed = sorted({att.kv_rows(it[3])[0] for its in merged.values() for it in its})
 
+    reference_copy()
     t0 = time.perf_counter()
     host = gen_inputs(w, owners, kv_needed, w.backward)
     q = {a: torch.from_numpy(host[0][a]).to(dev).to(td) for a in owners}
@@ -354,7 +318,7 @@ def main():
         o_part, l_part = partials[(a, kc)]
         for d, bs, src, rs in att.calls(a, kc):
             dfa.dfa_attn_fwd_partial(d, q[a][bs], k[src][bs, rs], v[src][bs, rs], o_part[bs],
-                                     l_part[bs])
+                                     l_part[bs], None, att.workspace(d, dfa.DFA_OP_FWD))
 
     def bwd_call(part):
         def call(it):
@@ -362,7 +326,8 @@ def main():
             for d, bs, src, rs in att.calls(a, kc):
                 dfa.dfa_test_bwd_part(d, q[a][bs], k[src][bs, rs], v[src][bs, rs], lse[a][bs],
                                       d_o[a][bs], delta[a][bs], dq[a][bs], dk[src][bs, rs],
-                                      dv[src][bs, rs], part)
+                                      dv[src][bs, rs], part, None,
+                                      att.workspace(d, dfa.DFA_OP_BWD))
         return call
 
     pairs_x_heads = n_pairs * w.batch * w.heads_q
@@ -402,6 +367,7 @@ def main():
                    "pairs_timed": len(timed), "backward": w.backward, "window": w.window,
                    "n_global": w.n_global,
                    "algorithmic_flop_per_step": flop, "wall_s_timed": round(wall, 3),
+                   "reference_copy_bytes": REFERENCE_COPY_BYTES,
                    "input_gen_s": round(gen_s, 1)},
         "roofline": roofline,
     }

@@ -19,12 +19,17 @@
  * scores of a row; a row that sees no key has O = 0 and LSE = -inf.
  *
  * Memory: every tensor pointer is DEVICE memory owned by the caller; the
- * library never allocates, frees or retains it.  Descriptors, work-item
- * arrays and the pointer arrays of dfa_lse_merge are HOST memory read
- * during the call only.
+ * library never allocates, frees or retains device memory of its own.
+ * Scratch that a call needs beyond its inputs and outputs (the forward's
+ * transposed V; the backward's row-split partials) is a caller-owned
+ * device workspace named in the descriptor (dfa_attn_desc.workspace /
+ * workspace_bytes), sized by dfa_attn_workspace_size.  Descriptors,
+ * work-item arrays and the pointer arrays of dfa_lse_merge are HOST memory
+ * read during the call only.
  *
  * Asynchrony: work is enqueued on `hip_stream` (a hipStream_t; NULL = the
- * null stream) and the call returns after enqueueing.  Nothing synchronises.
+ * null stream) and the call returns after enqueueing.  No call
+ * synchronises the host with the device, allocates or frees memory.
  *
  * Errors: arguments are checked before anything is enqueued; on a non-OK
  * status nothing was enqueued (except DFA_ERR_HIP, where a launch failed)
@@ -32,7 +37,13 @@
  * The schedules and all argument checks never touch the HIP runtime, so
  * they work on a machine without a GPU.
  *
- * Thread safety: every call is stateless and may be made from any thread.
+ * Thread safety: the library keeps no state between calls (apart from the
+ * calling thread's last error message) and every call may be made from any
+ * thread.  A call may enqueue several kernels that pass data through its
+ * workspace, so calls that share one workspace must be ordered: issued by
+ * one thread on one stream, or on streams ordered with events.  Calls with
+ * separate workspaces may be issued concurrently from any threads, on one
+ * stream or several.
  */
 #ifndef DFA_H
 #define DFA_H
@@ -48,13 +59,16 @@ typedef enum {
   DFA_ERR_INVALID = 1,      /* malformed argument (null pointer, bad shape) */
   DFA_ERR_UNSUPPORTED = 2,  /* well-formed but not implemented (head_dim, */
                             /* head counts past the 32-bit tile offsets)  */
-  DFA_ERR_CAPACITY = 3,     /* output array too small; required size given  */
+  DFA_ERR_CAPACITY = 3,     /* output array or workspace too small; the    */
+                            /* required size is given                       */
   DFA_ERR_HIP = 4           /* the HIP runtime reported an error            */
 } dfa_status;
 
 /* Element type of Q, K, V, dO and the final O.  DFA_BF16: bf16 matrix-core
  * products with fp32 accumulation.  DFA_F32: the exact path; fp32 in and
- * out, scores, exponentials and sums carried in fp64. */
+ * out, scores, exponentials and sums carried in fp64.  Across the ABI a
+ * dtype travels as an int32_t holding one of these values (a caller may
+ * put any integer there; the library checks it before using it). */
 typedef enum { DFA_F32 = 0, DFA_BF16 = 1 } dfa_dtype;
 
 /* One chunk pair of a schedule.  kind: 0 = diagonal pair (q_chunk ==
@@ -82,13 +96,36 @@ typedef struct {
   int32_t causal;       /* 1: key j visible to query i iff
                                kv_start + j <= q_start + i; 0: all visible */
   float scale;          /* score scale sigma (1/sqrt(head_dim)), finite    */
-  dfa_dtype dtype;      /* element type of Q, K, V, O (final) and dO       */
+  int32_t dtype;        /* a dfa_dtype: element type of Q, K, V, O (final)
+                           and dO                                          */
   int64_t window;       /* 0: no window.  > 0 (needs causal = 1): local
                            sliding window, key j visible to query i only if
                            (q_start + i) - (kv_start + j) < window, i.e. a
                            query sees itself and the window - 1 tokens
                            before it ([DistFlashAttn App. F])             */
+  void* workspace;      /* caller-owned DEVICE scratch for the call, 16-byte
+                           aligned, not overlapping any tensor argument;
+                           NULL allowed when dfa_attn_workspace_size gives 0 */
+  int64_t workspace_bytes; /* its size; a call that needs more returns
+                           DFA_ERR_CAPACITY (nothing enqueued)            */
 } dfa_attn_desc;
+
+/* The two descriptor calls whose kernels may need scratch. */
+typedef enum { DFA_OP_FWD = 0, DFA_OP_BWD = 1 } dfa_op;
+
+/* Device workspace (bytes) that dfa_attn_fwd_partial (op = DFA_OP_FWD) or
+ * dfa_attn_bwd (op = DFA_OP_BWD) needs for `desc` (its workspace fields are
+ * ignored here).  A pure function of the descriptor's shape, mask and dtype:
+ * computed on the host, no HIP call, the same on every device.
+ *   forward, bf16: the transposed V (2 * batch * heads_kv * head_dim bytes per
+ *     key, keys rounded up to 128); float32: 0.
+ *   backward, bf16: the fp32 dK/dV partials of the row split (0 unless a
+ *     few key blocks carry most of the pair's query rows, e.g. a short key
+ *     range or a window band); float32: 0.
+ * Each call writes and reads its workspace in stream order and leaves
+ * nothing in it that a later call reads. */
+dfa_status dfa_attn_workspace_size(const dfa_attn_desc* desc, int32_t op,
+                                   int64_t* bytes);
 
 /* Chunk-pair schedule of P = num_workers workers over P contiguous chunks
  * ([DistFlashAttn §3.2 and Fig. 3; App. B, Figs. 5-6]).
@@ -150,11 +187,7 @@ dfa_status dfa_global_window_schedule(int32_t num_workers, int64_t chunk_len,
  *   after a query tile's last row are skipped (§2, §3.2), and with a
  *   window so are key tiles entirely outside every window of the tile's
  *   rows (App. F).  For bf16 inputs the call first writes a transposed copy
- *   of v into a scratch buffer the library owns, one per device and stream
- *   (allocated on first use, grown on demand after the stream's earlier work
- *   has finished, kept until the process ends): calls on one stream are
- *   ordered, and calls on different streams use different buffers and may
- *   run concurrently. */
+ *   of v into desc->workspace (dfa_attn_workspace_size, DFA_OP_FWD). */
 dfa_status dfa_attn_fwd_partial(const dfa_attn_desc* desc, const void* q,
                                 const void* k, const void* v, float* o_part,
                                 float* lse, void* hip_stream);
@@ -167,13 +200,13 @@ dfa_status dfa_attn_fwd_partial(const dfa_attn_desc* desc, const void* q,
  *   rows with every LSE_r = -inf give O = 0, LSE = -inf.
  * o_parts / lse_parts: HOST arrays of n DEVICE pointers to float32
  * [batch,len_q,heads,head_dim] / [batch,heads,len_q].  o_out is written in
- * out_dtype, lse_out in float32.  o_out may alias o_parts[0] only when
+ * out_dtype (a dfa_dtype), lse_out in float32.  o_out may alias o_parts[0] only when
  * out_dtype == DFA_F32 (each element is read before it is written);
  * lse_out may alias lse_parts[0].  1 <= n <= 64. */
 dfa_status dfa_lse_merge(int32_t n, const float* const* o_parts,
                          const float* const* lse_parts, int32_t batch,
                          int32_t heads, int64_t len_q, int32_t head_dim,
-                         dfa_dtype out_dtype, void* o_out, float* lse_out,
+                         int32_t out_dtype, void* o_out, float* lse_out,
                          void* hip_stream);
 
 /* Backward of one chunk pair from the SAVED final output and LSE; the
@@ -193,14 +226,26 @@ dfa_status dfa_lse_merge(int32_t n, const float* const* o_parts,
  * to their owners).  Each call is deterministic.  When few key blocks carry
  * most of the pair's rows (a short key range against a long query chunk, a
  * window band) the dK/dV part splits each block's rows over several
- * workgroups and sums their partials in a fixed order, in the library's
- * scratch buffer of the call's stream (the one dfa_attn_fwd_partial uses:
- * one per device and stream, so calls on different streams may overlap). */
+ * workgroups and sums their partials in a fixed order in desc->workspace
+ * (dfa_attn_workspace_size, DFA_OP_BWD).  delta is computed whenever
+ * compute_delta is 1 and the pair has query rows, also when len_kv is 0. */
 dfa_status dfa_attn_bwd(const dfa_attn_desc* desc, const void* q,
                         const void* k, const void* v, const void* o,
                         const float* lse, const void* d_o, float* delta,
                         int32_t compute_delta, float* dq, float* dk,
                         float* dv, void* hip_stream);
+
+/* Emulated exchange of one step on a single device ([DistFlashAttn §3.2]:
+ * the next key/value chunk reaches a worker by peer-to-peer communication
+ * and is prefetched on a separate stream while the current pair computes;
+ * a helper's partial output and LSE travel back the same way).  Copies
+ * `bytes` bytes from device memory src to device memory dst on a DMA
+ * engine (hipMemcpyDeviceToDeviceNoCU), so the transfer takes no compute
+ * units from the attention kernels, as a link transfer would not.
+ * Enqueued on hip_stream; bytes >= 0 (0: nothing); dst and src non-null
+ * when bytes > 0 and not overlapping (else DFA_ERR_INVALID). */
+dfa_status dfa_chunk_transfer(void* dst, const void* src, int64_t bytes,
+                              void* hip_stream);
 
 /* Message of the last non-OK status on the calling thread ("" if none). */
 const char* dfa_last_error(void);
@@ -234,20 +279,6 @@ dfa_status dfa_test_bwd_part(const dfa_attn_desc* desc, const void* q,
                              float* dk, float* dv, int32_t part,
                              void* hip_stream);
 
-/* Matrix-core calibration: `workgroups` workgroups of 4 waves, every wave
- * running 4 independent chains of iters bf16 32x32x16 matrix products
- * (v_mfma_f32_32x32x16_bf16, 32768 FLOP each: 2^19 * workgroups * iters FLOP
- * per call) on register operands, with no memory traffic.  mode bit 0 set:
- * pseudo-random operand bits that keep switching, as real data does; clear:
- * one constant operand pair.  mode bit 1 set: the accumulators live in the
- * accumulation registers (AGPRs); clear: wherever the compiler puts them.
- * Other bits must be 0.  Timed over several seconds it gives the dense bf16
- * rate the board sustains under its power and current limits.
- * sink: DEVICE buffer of >= workgroups * 256 floats (practically never
- * written).  iters even, >= 2; workgroups in [1, 65536]. */
-dfa_status dfa_test_mfma_loop(int32_t workgroups, int32_t iters,
-                              int32_t mode, float* sink,
-                              void* hip_stream);
 
 #ifdef __cplusplus
 }

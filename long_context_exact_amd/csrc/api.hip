@@ -60,6 +60,19 @@ dfa_status need(const std::string& fn, const void* p, const char* name, bool vec
   return DFA_OK;
 }
 
+// The caller's workspace must hold what the call needs (checked before any
+// enqueue): DFA_ERR_CAPACITY names the required size.
+dfa_status check_workspace(const std::string& fn, const dfa_attn_desc& d, int64_t need_bytes) {
+  if (need_bytes <= 0) return DFA_OK;
+  if (d.workspace_bytes < need_bytes || d.workspace == nullptr)
+    return fail(DFA_ERR_CAPACITY, fn + ": workspace of " + std::to_string(need_bytes) +
+                                      " bytes required (dfa_attn_workspace_size), " +
+                                      std::to_string(d.workspace == nullptr ? 0 : d.workspace_bytes) +
+                                      " given");
+  if (!aligned16(d.workspace)) return fail(DFA_ERR_INVALID, fn + ": workspace must be 16-byte aligned");
+  return DFA_OK;
+}
+
 #define DFA_TRY(expr)                    \
   do {                                   \
     const dfa_status _st = (expr);       \
@@ -84,6 +97,7 @@ dfa_status fwd_common(const char* fn, const dfa_attn_desc* desc, const void* q, 
   }
   DFA_TRY(need(f, k, "k", true));
   DFA_TRY(need(f, v, "v", true));
+  DFA_TRY(check_workspace(f, d, fwd_workspace_bytes(d)));
   return launch_fwd(d, q, k, v, o_part, lse, visits, s);
 }
 
@@ -104,7 +118,7 @@ extern "C" dfa_status dfa_attn_fwd_partial(const dfa_attn_desc* desc, const void
 
 extern "C" dfa_status dfa_lse_merge(int32_t n, const float* const* o_parts,
                                     const float* const* lse_parts, int32_t batch, int32_t heads,
-                                    int64_t len_q, int32_t head_dim, dfa_dtype out_dtype,
+                                    int64_t len_q, int32_t head_dim, int32_t out_dtype,
                                     void* o_out, float* lse_out, void* hip_stream) {
   try {
     const std::string f("dfa_lse_merge");
@@ -151,18 +165,24 @@ dfa_status bwd_common(const char* fn, const dfa_attn_desc* desc, const void* q, 
   const dfa_attn_desc& d = *desc;
   if (compute_delta != 0 && compute_delta != 1)
     return fail(DFA_ERR_INVALID, f + ": compute_delta must be 0 or 1");
-  if (d.batch == 0 || d.len_q == 0 || d.len_kv == 0) return DFA_OK;  // nothing to add
+  if (d.batch == 0 || d.len_q == 0) return DFA_OK;  // no query rows: nothing to write
+  DFA_TRY(need(f, d_o, "d_o", true));
+  DFA_TRY(need(f, delta, "delta", false));
+  if (compute_delta) DFA_TRY(need(f, o, "o", true));
+  const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (d.len_kv == 0) {
+    // No keys: nothing to add to dq, dk, dv, but delta (which later pairs of
+    // the query chunk read) is still written when asked for.
+    return compute_delta ? launch_delta(d, o, d_o, delta, s) : DFA_OK;
+  }
   DFA_TRY(need(f, q, "q", true));
   DFA_TRY(need(f, k, "k", true));
   DFA_TRY(need(f, v, "v", true));
-  DFA_TRY(need(f, d_o, "d_o", true));
   DFA_TRY(need(f, lse, "lse", false));
-  DFA_TRY(need(f, delta, "delta", false));
   if (parts & 2) DFA_TRY(need(f, dq, "dq", true));
   if (parts & 1) DFA_TRY(need(f, dk, "dk", true));
   if (parts & 1) DFA_TRY(need(f, dv, "dv", true));
-  if (compute_delta) DFA_TRY(need(f, o, "o", true));
-  const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (parts & 1) DFA_TRY(check_workspace(f, d, bwd_workspace_bytes(d)));
   if (compute_delta) DFA_TRY(launch_delta(d, o, d_o, delta, s));
   return launch_bwd(d, q, k, v, lse, d_o, delta, dq, dk, dv, s, parts);
 }
@@ -195,23 +215,24 @@ extern "C" dfa_status dfa_test_bwd_part(const dfa_attn_desc* desc, const void* q
   }
 }
 
-extern "C" dfa_status dfa_test_mfma_loop(int32_t workgroups, int32_t iters,
-                                         int32_t mode, float* sink,
-                                         void* hip_stream) {
+extern "C" dfa_status dfa_attn_workspace_size(const dfa_attn_desc* desc, int32_t op,
+                                              int64_t* bytes) {
   try {
-    if (workgroups < 1 || workgroups > 65536 || iters < 2 || iters % 2 != 0)
-      return fail(DFA_ERR_INVALID,
-                  "dfa_test_mfma_loop: workgroups in [1, 65536], iters even and >= 2");
-    if (mode < 0 || mode > 3) return fail(DFA_ERR_INVALID, "dfa_test_mfma_loop: mode in [0, 3]");
-    if (sink == nullptr) return fail(DFA_ERR_INVALID, "dfa_test_mfma_loop: sink is null");
-    return launch_mfma_loop(workgroups, iters, mode, sink,
-                            static_cast<hipStream_t>(hip_stream));
+    DFA_TRY(check_desc("dfa_attn_workspace_size", desc));
+    if (bytes == nullptr) return fail(DFA_ERR_INVALID, "dfa_attn_workspace_size: bytes is null");
+    if (op == DFA_OP_FWD)
+      *bytes = fwd_workspace_bytes(*desc);
+    else if (op == DFA_OP_BWD)
+      *bytes = bwd_workspace_bytes(*desc);
+    else
+      return fail(DFA_ERR_INVALID, "dfa_attn_workspace_size: op must be DFA_OP_FWD or DFA_OP_BWD");
+    return DFA_OK;
   } catch (...) {
-    return fail(DFA_ERR_INVALID, "dfa_test_mfma_loop: internal error");
+    return fail(DFA_ERR_INVALID, "dfa_attn_workspace_size: internal error");
   }
 }
 
-extern "C" int32_t dfa_version(void) { return 100; }
+extern "C" int32_t dfa_version(void) { return 10000; }
 
 extern "C" dfa_status dfa_test_tile_shape(const dfa_attn_desc* desc, int32_t* bm, int32_t* bn) {
   DFA_TRY(check_desc("dfa_test_tile_shape", desc));

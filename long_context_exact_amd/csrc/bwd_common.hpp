@@ -62,6 +62,15 @@ __device__ __forceinline__ float lse2_of(float lse) {
 #define DFA_BWD_OCC 2  // waves per SIMD the register budget is sized for
 #endif
 
+// The kernels' arguments for a descriptor (pointers left null).
+BwdArgs bwd_args_of(const dfa_attn_desc& d);
+
+// Row-split workspace of the dK/dV kernel: bytes of one slice's fp32 dK and
+// dV partials, and the whole workspace the descriptor's split needs (0 when
+// it does not split).
+int64_t dkdv_split_bytes_per_slice(const dfa_attn_desc& d);
+int64_t dkdv_workspace_bytes(const dfa_attn_desc& d);
+
 // Launchers of the two kernels (head_dim 64 or 128, bf16 operands).
 dfa_status launch_dkdv_bf16(const dfa_attn_desc& d, const BwdArgs& a, hipStream_t s);
 dfa_status launch_dq_bf16(const dfa_attn_desc& d, const BwdArgs& a, hipStream_t s);

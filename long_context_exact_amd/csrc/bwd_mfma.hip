@@ -32,21 +32,8 @@ dfa_status launch_bwd_f32(const dfa_attn_desc& d, const void* q, const void* k, 
                           const float* lse, const void* d_o, const float* delta, float* dq,
                           float* dk, float* dv, hipStream_t s, int parts);
 
-dfa_status launch_bwd(const dfa_attn_desc& d, const void* q, const void* k, const void* v,
-                      const float* lse, const void* d_o, const float* delta, float* dq,
-                      float* dk, float* dv, hipStream_t s, int parts) {
-  if (d.dtype == DFA_F32)
-    return launch_bwd_f32(d, q, k, v, lse, d_o, delta, dq, dk, dv, s, parts);
+BwdArgs bwd_args_of(const dfa_attn_desc& d) {
   BwdArgs a{};
-  a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v);
-  a.d_o = static_cast<const uint16_t*>(d_o);
-  a.lse = lse;
-  a.delta = delta;
-  a.dq = dq;
-  a.dk = dk;
-  a.dv = dv;
   a.len_q = d.len_q;
   a.len_kv = d.len_kv;
   a.q_start = d.q_start;
@@ -63,6 +50,29 @@ dfa_status launch_bwd(const dfa_attn_desc& d, const void* q, const void* k, cons
   a.win = d.window > 0 ? d.window : kNoWindow;
   a.rsplit = 1;  // the dK/dV launcher may split rows
   a.ws = nullptr;
+  return a;
+}
+
+int64_t bwd_workspace_bytes(const dfa_attn_desc& d) {
+  if (d.dtype != DFA_BF16) return 0;
+  return dkdv_workspace_bytes(d);
+}
+
+dfa_status launch_bwd(const dfa_attn_desc& d, const void* q, const void* k, const void* v,
+                      const float* lse, const void* d_o, const float* delta, float* dq,
+                      float* dk, float* dv, hipStream_t s, int parts) {
+  if (d.dtype == DFA_F32)
+    return launch_bwd_f32(d, q, k, v, lse, d_o, delta, dq, dk, dv, s, parts);
+  BwdArgs a = bwd_args_of(d);
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.d_o = static_cast<const uint16_t*>(d_o);
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
   if (parts & 1) {
     const dfa_status st = launch_dkdv_bf16(d, a, s);
     if (st != DFA_OK) return st;

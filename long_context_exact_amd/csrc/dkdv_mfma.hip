@@ -327,41 +327,43 @@ __global__ __launch_bounds__(256) void dkdv_split_reduce_kernel(BwdArgs a, int64
 constexpr int kDkvNW = 8;
 constexpr int kMaxSplit = 64;                                // slices per key block
 constexpr int kMinSplitSteps = 32;                           // steps per slice, at least
-constexpr size_t kMaxSplitBytes = size_t(4) << 30;           // workspace cap
+constexpr int64_t kMaxSplitBytes = int64_t(4) << 30;         // workspace cap
+// The split plan is sized for the MI355X's 256 compute units rather than
+// queried from the device, so that it (and the workspace it needs) is a pure
+// function of the descriptor, known on the host before any HIP call.
+constexpr int64_t kSplitCUs = 256;
+
+// Slices per key block of the row split (1: no split).  Split when the
+// longest key block's steps exceed twice an even share of all steps over the
+// compute units (few key blocks with many rows: a short key range such as
+// global tokens, or the blocks a window band reaches).
+template <int D>
+int dkdv_row_split(const dfa_attn_desc& d) {
+  using C = DkvCfg<D, kDkvNW>;
+  const BwdArgs a = bwd_args_of(d);
+  const int64_t nkb = cdiv(d.len_kv, C::BK);
+  int64_t total = 0, longest = 0;
+  for (int64_t kb = 0; kb < nkb; ++kb) {
+    const int st = dkdv_span(a, kb * C::BK, C::BK, C::BQ).steps;
+    total += st;
+    longest = std::max<int64_t>(longest, st);
+  }
+  total *= int64_t(d.heads_kv) * d.batch;
+  const int64_t share = std::max<int64_t>(1, cdiv(total, kSplitCUs));
+  int64_t split = longest > 2 * share ? cdiv(longest, share) : 1;
+  split = std::min<int64_t>({split, kMaxSplit, std::max<int64_t>(1, longest / kMinSplitSteps)});
+  split = std::min<int64_t>(split, kMaxSplitBytes / dkdv_split_bytes_per_slice(d));
+  return int(std::max<int64_t>(split, 1));
+}
 
 template <int D>
 dfa_status launch_dkdv(const dfa_attn_desc& d, BwdArgs a, hipStream_t s) {
   using C = DkvCfg<D, kDkvNW>;
-  // Row split: when the longest key block's steps exceed twice an even
-  // share of all steps over the CUs (few key blocks with many rows: a short
-  // key range such as global tokens, or the blocks a window band reaches),
-  // cut every block's steps into slices that run as separate workgroups.
   const int64_t nkb = cdiv(d.len_kv, C::BK);
-  a.rsplit = 1;
-  a.ws = nullptr;
-  {
-    int64_t total = 0, longest = 0;
-    for (int64_t kb = 0; kb < nkb; ++kb) {
-      const int st = dkdv_span(a, kb * C::BK, C::BK, C::BQ).steps;
-      total += st;
-      longest = std::max<int64_t>(longest, st);
-    }
-    total *= int64_t(d.heads_kv) * d.batch;
-    int dev = 0, cus = 0;  // the current device's compute units (a cheap attribute query)
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-      cus = 256;
-    const int64_t share = std::max<int64_t>(1, cdiv(total, cus));
-    int64_t split = longest > 2 * share ? cdiv(longest, share) : 1;
-    split = std::min<int64_t>({split, kMaxSplit, std::max<int64_t>(1, longest / kMinSplitSteps)});
-    const size_t per = size_t(2) * d.batch * d.len_kv * d.heads_kv * D * sizeof(float);
-    split = std::min<int64_t>(split, int64_t(kMaxSplitBytes / per));
-    if (split > 1) {
-      a.ws = static_cast<float*>(device_workspace(size_t(split) * per, s));
-      if (a.ws != nullptr) a.rsplit = int32_t(split);
-    }
-  }
+  // Row split into the caller's workspace (sized by bwd_workspace_bytes and
+  // checked before this call).
+  a.rsplit = dkdv_row_split<D>(d);
+  a.ws = a.rsplit > 1 ? static_cast<float*>(d.workspace) : nullptr;
   dim3 grid(unsigned(nkb) * unsigned(d.heads_kv), unsigned(d.batch), unsigned(a.rsplit));
   auto go = [&](auto kern) {
     const dfa_status st = allow_lds(kern, C::LDS_BYTES, "dkdv_bf16_kernel");
@@ -386,6 +388,16 @@ dfa_status launch_dkdv(const dfa_attn_desc& d, BwdArgs a, hipStream_t s) {
 dfa_status launch_dkdv_bf16(const dfa_attn_desc& d, const BwdArgs& a, hipStream_t s) {
   if (d.head_dim == 128) return launch_dkdv<128>(d, a, s);
   return launch_dkdv<64>(d, a, s);
+}
+
+int64_t dkdv_split_bytes_per_slice(const dfa_attn_desc& d) {
+  return int64_t(2) * d.batch * d.len_kv * d.heads_kv * d.head_dim * int64_t(sizeof(float));
+}
+
+int64_t dkdv_workspace_bytes(const dfa_attn_desc& d) {
+  if (d.batch == 0 || d.len_q == 0 || d.len_kv == 0) return 0;
+  const int split = d.head_dim == 128 ? dkdv_row_split<128>(d) : dkdv_row_split<64>(d);
+  return split > 1 ? split * dkdv_split_bytes_per_slice(d) : 0;
 }
 
 }  // namespace dfa

@@ -21,7 +21,7 @@
 //   16 accumulator registers plus the lane 32 apart;
 //   O^T += V^T P^T     (A = V^T rows from LDS, B = P^T straight from the S^T
 //   accumulators).  Before the kernel, V is transposed once per call into
-//   library scratch, V^T [B][Hkv][d][keys], with the keys of every 16-key
+//   the caller's workspace, V^T [B][Hkv][d][keys], with the keys of every 16-key
 //   group stored in the order the accumulator layout hands P^T over (bits 2
 //   and 3 of the key index swapped), so each lane's A fragment is 8
 //   consecutive elements of a V^T row: a 16-byte read instead of two
@@ -329,6 +329,12 @@ dfa_status launch_d(const dfa_attn_desc& d, const FwdArgs& a, bool instr, hipStr
 dfa_status launch_fwd_f32(const dfa_attn_desc& d, const void* q, const void* k, const void* v,
                           float* o, float* lse, hipStream_t s);
 
+// The transposed V: [B][Hkv][d][keys rounded up to a whole key tile] bf16.
+int64_t fwd_workspace_bytes(const dfa_attn_desc& d) {
+  if (d.dtype != DFA_BF16 || d.batch == 0 || d.len_q == 0 || d.len_kv == 0) return 0;
+  return int64_t(d.batch) * d.heads_kv * d.head_dim * (cdiv(d.len_kv, kBN) * kBN) * 2;
+}
+
 void fwd_tile_shape(const dfa_attn_desc& d, int32_t* bm, int32_t* bn) {
   if (d.dtype == DFA_F32) {  // exact fp32 kernel: one row per wave, all keys
     *bm = 4;
@@ -362,16 +368,13 @@ dfa_status launch_fwd(const dfa_attn_desc& d, const void* q, const void* k, cons
   // every visible key the weight exp2(0) = 1 in fp32.
   a.c = std::max(d.scale * kLog2e, FLT_MIN);
   a.win = d.window > 0 ? d.window : kNoWindow;
-  // V^T into library scratch (stream-ordered before the forward kernel)
+  // V^T into the caller's workspace (stream-ordered before the forward kernel;
+  // its size was checked against fwd_workspace_bytes before this call)
   a.vt_ld = cdiv(d.len_kv, kBN) * kBN;
   if (uint64_t(a.vt_ld) * 2 * uint64_t(d.head_dim) >= (uint64_t(1) << 32))
     return fail(DFA_ERR_UNSUPPORTED, "dfa_attn_fwd_partial: len_kv too large for 32-bit V^T offsets");
   if (a.vt_ld > 0) {
-    const size_t bytes = size_t(d.batch) * d.heads_kv * d.head_dim * size_t(a.vt_ld) * 2;
-    uint16_t* vt = static_cast<uint16_t*>(device_workspace(bytes, s));
-    if (vt == nullptr)
-      return fail(DFA_ERR_HIP, "dfa_attn_fwd_partial: cannot allocate " + std::to_string(bytes) +
-                                   " bytes of V^T scratch");
+    uint16_t* vt = static_cast<uint16_t*>(d.workspace);
     const dfa_status st = launch_kv_transpose(static_cast<const uint16_t*>(v), vt, d.batch,
                                               d.len_kv, d.heads_kv, d.head_dim, a.vt_ld, s);
     if (st != DFA_OK) return st;

@@ -15,7 +15,7 @@ void fwd_tile_shape(const dfa_attn_desc& d, int32_t* bm, int32_t* bn);
 dfa_status launch_merge(int32_t n, const float* const* o_parts,
                         const float* const* lse_parts, int32_t batch,
                         int32_t heads, int64_t len_q, int32_t head_dim,
-                        dfa_dtype out_dtype, void* o_out, float* lse_out,
+                        int32_t out_dtype, void* o_out, float* lse_out,
                         hipStream_t s);
 
 dfa_status launch_delta(const dfa_attn_desc& d, const void* o, const void* d_o,
@@ -52,23 +52,16 @@ inline bool pair_is_full(const dfa_attn_desc& d, int64_t tile) {
   return all_visible && in_window && d.len_kv % tile == 0;
 }
 
-// Library-owned device scratch of at least `bytes` for work enqueued on
-// `stream` (one buffer per device and stream: the calls on a stream are
-// ordered, calls on different streams use different buffers); nullptr if it
-// cannot be allocated.
-void* device_workspace(size_t bytes, hipStream_t stream);
+// Device workspace (bytes) the forward / backward of a descriptor needs:
+// host arithmetic only (no HIP call), so the size query works anywhere.
+int64_t fwd_workspace_bytes(const dfa_attn_desc& d);
+int64_t bwd_workspace_bytes(const dfa_attn_desc& d);
 
 // X [B][len][H][d] bf16 -> X^T [B][H][d][ld] (ld a multiple of 64, >= len):
 // keys permuted within 16-key groups (index bits 2 and 3 swapped), keys past
 // len zero.  The layout the forward reads V^T from for O^T += V^T P^T.
 dfa_status launch_kv_transpose(const uint16_t* x, uint16_t* xt, int32_t batch, int64_t len,
                                int32_t heads, int32_t head_dim, int64_t ld, hipStream_t s);
-
-// Matrix-core calibration loop (test support): `workgroups` workgroups of
-// 4 waves, each wave 4 chains of `iters` / 2 x 2 bf16 32x32x16 products;
-// sink holds >= workgroups * 256 floats.
-dfa_status launch_mfma_loop(int32_t workgroups, int32_t iters, int32_t mode, float* sink,
-                            hipStream_t s);
 
 // o = 0, lse = -inf for every row (a chunk pair with no keys).
 dfa_status launch_fill_empty(int64_t n_o, float* o, int64_t n_lse, float* lse,

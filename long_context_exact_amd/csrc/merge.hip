@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) void fill_kernel(float* o, int64_t n_o, float*
 
 dfa_status launch_merge(int32_t n, const float* const* o_parts, const float* const* lse_parts,
                         int32_t batch, int32_t heads, int64_t len_q, int32_t head_dim,
-                        dfa_dtype out_dtype, void* o_out, float* lse_out, hipStream_t s) {
+                        int32_t out_dtype, void* o_out, float* lse_out, hipStream_t s) {
   MergeArgs a{};
   for (int r = 0; r < n; ++r) {
     a.o[r] = o_parts[r];

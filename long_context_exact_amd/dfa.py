@@ -21,6 +21,7 @@ from .build import LIB_PATH
 
 DFA_OK, DFA_ERR_INVALID, DFA_ERR_UNSUPPORTED, DFA_ERR_CAPACITY, DFA_ERR_HIP = range(5)
 DFA_F32, DFA_BF16 = 0, 1
+DFA_OP_FWD, DFA_OP_BWD = 0, 1
 DIAG, FULL, BAND, GLOBAL = 0, 1, 2, 3
 
 _DTYPES = {"f32": DFA_F32, "bf16": DFA_BF16}
@@ -28,9 +29,10 @@ _TORCH = {DFA_F32: torch.float32, DFA_BF16: torch.bfloat16}
 
 EXPORTED = (
     "dfa_balanced_schedule", "dfa_window_schedule", "dfa_global_window_schedule",
-    "dfa_attn_fwd_partial", "dfa_lse_merge", "dfa_attn_bwd",
+    "dfa_attn_fwd_partial", "dfa_lse_merge", "dfa_attn_bwd", "dfa_attn_workspace_size",
+    "dfa_chunk_transfer",
     "dfa_last_error", "dfa_version", "dfa_test_tile_shape", "dfa_test_fwd_tile_visits",
-    "dfa_test_bwd_part", "dfa_test_mfma_loop",
+    "dfa_test_bwd_part",
 )
 
 
@@ -53,6 +55,7 @@ class AttnDesc(ctypes.Structure):
         ("head_dim", ctypes.c_int32), ("len_q", ctypes.c_int64), ("len_kv", ctypes.c_int64),
         ("q_start", ctypes.c_int64), ("kv_start", ctypes.c_int64), ("causal", ctypes.c_int32),
         ("scale", ctypes.c_float), ("dtype", ctypes.c_int32), ("window", ctypes.c_int64),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64),
     ]
 
 
@@ -92,11 +95,13 @@ def lib() -> ctypes.CDLL:
         L.dfa_test_fwd_tile_visits.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P]
         L.dfa_test_bwd_part.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, P, P, I32,
                                         P]
-        L.dfa_test_mfma_loop.argtypes = [I32, I32, I32, P, P]
+        L.dfa_attn_workspace_size.argtypes = [ctypes.POINTER(AttnDesc), I32, ctypes.POINTER(I64)]
+        L.dfa_chunk_transfer.argtypes = [P, P, I64, P]
         for name in ("dfa_balanced_schedule", "dfa_window_schedule", "dfa_global_window_schedule",
-                     "dfa_attn_fwd_partial", "dfa_lse_merge",
+                     "dfa_attn_fwd_partial", "dfa_lse_merge", "dfa_attn_workspace_size",
+                     "dfa_chunk_transfer",
                      "dfa_attn_bwd", "dfa_test_tile_shape", "dfa_test_fwd_tile_visits",
-                     "dfa_test_bwd_part", "dfa_test_mfma_loop"):
+                     "dfa_test_bwd_part"):
             getattr(L, name).restype = I32
         L.dfa_last_error.argtypes = []
         L.dfa_last_error.restype = ctypes.c_char_p
@@ -117,6 +122,14 @@ def _stream(stream):
     if isinstance(stream, torch.cuda.Stream):
         return ctypes.c_void_p(stream.cuda_stream)
     return ctypes.c_void_p(int(stream))
+
+
+def _torch_stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream))
 
 
 def _ptr(t, name, shape, dtype):
@@ -145,6 +158,36 @@ def _shapes(d: AttnDesc):
     ks = (d.batch, d.len_kv, d.heads_kv, d.head_dim)
     ls = (d.batch, d.heads_q, d.len_q)
     return qs, ks, ls
+
+
+def dfa_attn_workspace_size(desc: AttnDesc, op: int) -> int:
+    """Bytes of device workspace dfa_attn_fwd_partial (DFA_OP_FWD) or
+    dfa_attn_bwd (DFA_OP_BWD) needs for `desc` (host arithmetic only)."""
+    n = ctypes.c_int64(0)
+    _check(lib().dfa_attn_workspace_size(ctypes.byref(desc), int(op), ctypes.byref(n)))
+    return int(n.value)
+
+
+def _with_workspace(desc: AttnDesc, op: int, workspace, stream):
+    """A copy of `desc` naming the caller's workspace (a uint8 device tensor),
+    and the tensor to keep alive over the call.  Without one, a workspace of
+    the required size is taken from torch's allocator on the call's stream, so
+    that torch hands its memory to later work of that stream only."""
+    d = AttnDesc.from_buffer_copy(desc)
+    if workspace is None:
+        need = dfa_attn_workspace_size(desc, op)
+        if need == 0:
+            d.workspace, d.workspace_bytes = None, 0
+            return d, None
+        s = _torch_stream(stream)
+        with torch.cuda.stream(s):
+            workspace = torch.empty(need, dtype=torch.uint8, device=s.device)
+    if not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8 or \
+            not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 torch tensor")
+    _ptr(workspace, "workspace", tuple(workspace.shape), torch.uint8)
+    d.workspace, d.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    return d, workspace
 
 
 def dfa_version() -> int:
@@ -199,12 +242,16 @@ def dfa_global_window_schedule(num_workers: int, chunk_len: int, window: int, n_
     return [arr[i].astuple() for i in range(n.value)], int(steps.value)
 
 
-def dfa_attn_fwd_partial(desc: AttnDesc, q, k, v, o_part, lse, stream=None):
+def dfa_attn_fwd_partial(desc: AttnDesc, q, k, v, o_part, lse, stream=None, workspace=None):
+    """workspace: a uint8 device tensor of at least
+    dfa_attn_workspace_size(desc, DFA_OP_FWD) bytes (taken from torch's
+    allocator for this call when None)."""
     qs, ks, ls = _shapes(desc)
     dt = _TORCH.get(desc.dtype, torch.bfloat16)
     args = (_ptr(q, "q", qs, dt), _ptr(k, "k", ks, dt), _ptr(v, "v", ks, dt),
             _ptr(o_part, "o_part", qs, torch.float32), _ptr(lse, "lse", ls, torch.float32))
-    _check(lib().dfa_attn_fwd_partial(ctypes.byref(desc), *args, _stream(stream)))
+    d, _keep = _with_workspace(desc, DFA_OP_FWD, workspace, stream)
+    _check(lib().dfa_attn_fwd_partial(ctypes.byref(d), *args, _stream(stream)))
 
 
 def dfa_lse_merge(o_parts: Sequence[torch.Tensor], lse_parts: Sequence[torch.Tensor], batch: int,
@@ -225,7 +272,10 @@ def dfa_lse_merge(o_parts: Sequence[torch.Tensor], lse_parts: Sequence[torch.Ten
 
 
 def dfa_attn_bwd(desc: AttnDesc, q, k, v, o, lse, d_o, delta, compute_delta: bool, dq, dk, dv,
-                 stream=None):
+                 stream=None, workspace=None):
+    """workspace: a uint8 device tensor of at least
+    dfa_attn_workspace_size(desc, DFA_OP_BWD) bytes (taken from torch's
+    allocator for this call when None and needed)."""
     qs, ks, ls = _shapes(desc)
     dt = _TORCH.get(desc.dtype, torch.bfloat16)
     f32 = torch.float32
@@ -233,7 +283,19 @@ def dfa_attn_bwd(desc: AttnDesc, q, k, v, o, lse, d_o, delta, compute_delta: boo
             _ptr(o, "o", qs, dt), _ptr(lse, "lse", ls, f32), _ptr(d_o, "d_o", qs, dt),
             _ptr(delta, "delta", ls, f32), int(bool(compute_delta)),
             _ptr(dq, "dq", qs, f32), _ptr(dk, "dk", ks, f32), _ptr(dv, "dv", ks, f32))
-    _check(lib().dfa_attn_bwd(ctypes.byref(desc), *args, _stream(stream)))
+    d, _keep = _with_workspace(desc, DFA_OP_BWD, workspace, stream)
+    _check(lib().dfa_attn_bwd(ctypes.byref(d), *args, _stream(stream)))
+
+
+def dfa_chunk_transfer(dst, src, stream=None):
+    """dst <- src (same shape and dtype, contiguous, on the current device)
+    on a DMA engine, enqueued on `stream`: the emulated exchange of a chunk."""
+    if not isinstance(src, torch.Tensor):
+        raise TypeError("src must be a torch.Tensor")
+    s_ptr = _ptr(src, "src", tuple(src.shape), src.dtype)
+    d_ptr = _ptr(dst, "dst", tuple(src.shape), src.dtype)
+    _check(lib().dfa_chunk_transfer(d_ptr, s_ptr, src.numel() * src.element_size(),
+                                    _stream(stream)))
 
 
 def dfa_test_tile_shape(desc: AttnDesc):
@@ -242,7 +304,8 @@ def dfa_test_tile_shape(desc: AttnDesc):
     return int(bm.value), int(bn.value)
 
 
-def dfa_test_fwd_tile_visits(desc: AttnDesc, q, k, v, o_part, lse, visits, stream=None):
+def dfa_test_fwd_tile_visits(desc: AttnDesc, q, k, v, o_part, lse, visits, stream=None,
+                             workspace=None):
     qs, ks, ls = _shapes(desc)
     bm, bn = dfa_test_tile_shape(desc)
     vshape = (-(-desc.len_q // bm), -(-desc.len_kv // bn))
@@ -250,11 +313,12 @@ def dfa_test_fwd_tile_visits(desc: AttnDesc, q, k, v, o_part, lse, visits, strea
     args = (_ptr(q, "q", qs, dt), _ptr(k, "k", ks, dt), _ptr(v, "v", ks, dt),
             _ptr(o_part, "o_part", qs, torch.float32), _ptr(lse, "lse", ls, torch.float32),
             _ptr(visits, "visits", vshape, torch.uint8))
-    _check(lib().dfa_test_fwd_tile_visits(ctypes.byref(desc), *args, _stream(stream)))
+    d, _keep = _with_workspace(desc, DFA_OP_FWD, workspace, stream)
+    _check(lib().dfa_test_fwd_tile_visits(ctypes.byref(d), *args, _stream(stream)))
 
 
 def dfa_test_bwd_part(desc: AttnDesc, q, k, v, lse, d_o, delta, dq, dk, dv, part: int,
-                      stream=None):
+                      stream=None, workspace=None):
     """One backward kernel alone (1: dK/dV, 2: dQ), delta already computed."""
     qs, ks, ls = _shapes(desc)
     dt = _TORCH.get(desc.dtype, torch.bfloat16)
@@ -264,15 +328,5 @@ def dfa_test_bwd_part(desc: AttnDesc, q, k, v, lse, d_o, delta, dq, dk, dv, part
             _ptr(dq, "dq", qs, f32) if part == 2 else None,
             _ptr(dk, "dk", ks, f32) if part == 1 else None,
             _ptr(dv, "dv", ks, f32) if part == 1 else None)
-    _check(lib().dfa_test_bwd_part(ctypes.byref(desc), *args, int(part), _stream(stream)))
-
-
-def dfa_test_mfma_loop(workgroups: int, iters: int, mode: int, sink, stream=None):
-    """Matrix-core calibration loop (2^19 * workgroups * iters bf16 FLOP);
-    mode bit 0: random operands, bit 1: accumulators in AGPRs."""
-    if not isinstance(sink, torch.Tensor) or sink.dtype != torch.float32 or \
-            sink.numel() < workgroups * 256:
-        raise ValueError("sink must be a float32 tensor of at least workgroups * 256 elements")
-    _check(lib().dfa_test_mfma_loop(int(workgroups), int(iters), int(mode),
-                                    _ptr(sink, "sink", tuple(sink.shape), torch.float32),
-                                    _stream(stream)))
+    d, _keep = _with_workspace(desc, DFA_OP_BWD, workspace, stream)
+    _check(lib().dfa_test_bwd_part(ctypes.byref(d), *args, int(part), _stream(stream)))

@@ -20,6 +20,13 @@ add into the same dK/dV rows.  On one GPU the workers are plain
 work items on one stream; a helper's returned (O, LSE) is simply a buffer
 the owner's merge reads.
 
+The scratch the kernels need (the forward's transposed V, the backward's
+row-split partials) is a workspace per device and stream that this object
+owns: a torch tensor grown to the largest size any call on that stream has
+asked for, passed to every call.  Calls on one stream are ordered, so they
+may share it; calls on different streams get different workspaces and may
+overlap.  The library itself allocates nothing.
+
 This module only sequences library calls; every number is computed by the
 library's kernels.
 """
@@ -62,6 +69,25 @@ class ChunkedCausalAttention:
             self.items, self.num_steps = dfa.dfa_balanced_schedule(self.workers, self.balanced)
         if self.scale is None:
             self.scale = self.head_dim ** -0.5
+        self._ws = {}
+
+    def workspace(self, desc: dfa.AttnDesc, op: int, device=None, stream=None):
+        """This object's workspace for calls on `stream` (None: the current
+        stream) of `device`, grown to what `desc` needs for `op`
+        (dfa.DFA_OP_FWD / DFA_OP_BWD).  It is allocated on that stream, so
+        when growing drops the old tensor torch reuses its memory only for
+        work queued after the calls already on that stream."""
+        dev = torch.device("cuda", torch.cuda.current_device()) if device is None else \
+            torch.device(device)
+        ts = dfa._torch_stream(stream)
+        key = (dev, ts.cuda_stream)
+        need = dfa.dfa_attn_workspace_size(desc, op)
+        ws = self._ws.get(key)
+        if ws is None or ws.numel() < need:
+            with torch.cuda.stream(ts):
+                ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+            self._ws[key] = ws
+        return ws
 
     # ---- schedule views -------------------------------------------------
     def items_of_worker(self, w: int):
@@ -123,7 +149,8 @@ class ChunkedCausalAttention:
             o_part, lse = partials[(a, c)]
             for d, bs, src, rs in self.calls(a, c):
                 dfa.dfa_attn_fwd_partial(d, q[a][bs], k[src][bs, rs], v[src][bs, rs], o_part[bs],
-                                         lse[bs], stream)
+                                         lse[bs], stream,
+                                         self.workspace(d, dfa.DFA_OP_FWD, q[a].device, stream))
 
     def merge_owner(self, a, partials, o_out, lse_out, stream=None):
         its = self.items_of_owner(a)
@@ -149,7 +176,8 @@ class ChunkedCausalAttention:
                 dfa.dfa_attn_bwd(d, q[a][bs], k[src][bs, rs], v[src][bs, rs],
                                  o[a][bs] if first else None, lse[a][bs], d_o[a][bs],
                                  delta[a][bs], first, dq[a][bs], dk[src][bs, rs],
-                                 dv[src][bs, rs], stream)
+                                 dv[src][bs, rs], stream,
+                                 self.workspace(d, dfa.DFA_OP_BWD, q[a].device, stream))
                 have.update((a, b) for b in rows)
         return have
 
@@ -163,10 +191,11 @@ class ChunkedCausalAttention:
         An owner item (w, c), c != w, needs chunk c's K and V from worker c;
         a helper item (a, w) needs owner a's Q and sends its (O, LSE) back.
         Each received tensor lands in one of two receive slots by a
-        device-to-device copy on the communication stream; the copy for step
-        t + 1 is issued before step t computes, and a slot is refilled only
-        after the compute that read it finished (events).  A helper's result
-        goes back to the owner's buffer on the communication stream.  With
+        DMA-engine copy (dfa_chunk_transfer: no compute units, as a link
+        transfer) on the communication stream; the copy for step t + 1 is
+        issued before step t computes, and a slot is refilled only after the
+        compute that read it finished (events).  A helper's result goes back
+        to the owner's buffer on the communication stream.  With
         overlap=False every copy runs on the compute stream, in line with
         the computation (the non-overlapped baseline).  Results are bitwise
         those of `forward_items`."""
@@ -195,10 +224,10 @@ class ChunkedCausalAttention:
                 if done[i % 2] is not None:
                     comm.wait_event(done[i % 2])
                 if a != w:      # helper: the owner's queries come in
-                    sl["q"].copy_(q[a], non_blocking=True)
+                    dfa.dfa_chunk_transfer(sl["q"], q[a], comm)
                 elif c != w:    # owner: the key/value chunk comes in
-                    sl["k"].copy_(k[c], non_blocking=True)
-                    sl["v"].copy_(v[c], non_blocking=True)
+                    dfa.dfa_chunk_transfer(sl["k"], k[c], comm)
+                    dfa.dfa_chunk_transfer(sl["v"], v[c], comm)
                 ev = torch.cuda.Event()
                 ev.record(comm)
                 ready[i] = ev
@@ -221,7 +250,9 @@ class ChunkedCausalAttention:
                 out = helper_out[hb]
             else:
                 out = partials[(a, c)]
-            dfa.dfa_attn_fwd_partial(self.desc(a, c), qa, kc, vc, *out)
+            d = self.desc(a, c)
+            dfa.dfa_attn_fwd_partial(d, qa, kc, vc, *out, None,
+                                     self.workspace(d, dfa.DFA_OP_FWD, dev))
             ev = torch.cuda.Event()
             ev.record(compute)
             done[i % 2] = ev
@@ -229,7 +260,7 @@ class ChunkedCausalAttention:
                 with torch.cuda.stream(comm):
                     comm.wait_event(ev)
                     for dst, src in zip(partials[(a, c)], out):
-                        dst.copy_(src, non_blocking=True)
+                        dfa.dfa_chunk_transfer(dst, src, comm)
                     back[hb] = torch.cuda.Event()
                     back[hb].record(comm)
                 nh += 1

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(dfa_lib):
 
 
 def test_version(dfa_lib):
-    assert dfa_lib.dfa_version() == 100
+    assert dfa_lib.dfa_version() == 10000
 
 
 @pytest.mark.parametrize("p", list(range(1, 65)) + [127, 128, 1000])
@@ -224,7 +224,9 @@ def test_runtime_without_device_reports_hip_error(dfa_lib):
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     L = dfa_lib.lib()
-    assert _fwd(L, D.make_desc(1, 2, 2, 64, 128, 128)) == D.DFA_ERR_HIP
+    d = D.make_desc(1, 2, 2, 64, 128, 128)
+    d.workspace, d.workspace_bytes = 1 << 24, 1 << 20
+    assert _fwd(L, d) == D.DFA_ERR_HIP
     assert dfa_lib.dfa_last_error()
 
 
@@ -236,10 +238,115 @@ def test_binding_rejects_mismatched_tensors(dfa_lib):
         dfa_lib.dfa_attn_fwd_partial(d, cpu, cpu, cpu, None, None)
 
 
-def test_mfma_loop_argument_errors(dfa_lib):
+def _ws_size(dfa_lib, d, op):
+    n = ctypes.c_int64(-1)
+    st = dfa_lib.lib().dfa_attn_workspace_size(ctypes.byref(d), op, ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_size_forward(dfa_lib):
+    """The forward's workspace is the transposed V: 2 bytes per element of
+    [B][Hkv][d][keys rounded up to 128]; nothing for fp32 or empty pairs."""
+    for b, hq, hkv, dh, lq, lk in ((1, 64, 8, 128, 32768, 32768), (2, 4, 2, 64, 100, 130),
+                                   (3, 6, 3, 128, 1, 1)):
+        d = D.make_desc(b, hq, hkv, dh, lq, lk)
+        st, n = _ws_size(dfa_lib, d, D.DFA_OP_FWD)
+        assert st == D.DFA_OK and n == 2 * b * hkv * dh * (-(-lk // 128) * 128)
+        assert dfa_lib.dfa_attn_workspace_size(d, D.DFA_OP_FWD) == n
+    assert dfa_lib.dfa_attn_workspace_size(D.make_desc(1, 2, 2, 64, 128, 128, dtype="f32"),
+                                           D.DFA_OP_FWD) == 0
+    assert dfa_lib.dfa_attn_workspace_size(D.make_desc(1, 2, 2, 64, 0, 128), D.DFA_OP_FWD) == 0
+    assert dfa_lib.dfa_attn_workspace_size(D.make_desc(1, 2, 2, 64, 16, 0), D.DFA_OP_FWD) == 0
+    assert dfa_lib.dfa_attn_workspace_size(D.make_desc(1, 64, 8, 128, 32768, 32768),
+                                           D.DFA_OP_FWD) == 64 << 20   # the 32K-chunk GQA pair
+
+
+def test_workspace_size_backward():
+    """The backward needs scratch only where dK/dV splits a key block's rows:
+    not on whole-chunk pairs, but on a short key range against a long query
+    chunk (the 1024 global keys against a 32768-row chunk: 8 slices of fp32
+    dK and dV) and on a window band."""
+    per = 2 * 1024 * 8 * 128 * 4          # one slice: fp32 dK and dV of 1024 keys x 8 heads
+    for lq, lk, qs, ks, win, want in ((32768, 32768, 15 * 32768, 14 * 32768, 0, 0),
+                                      (32768, 32768, 15 * 32768, 15 * 32768, 0, 0),
+                                      (32768, 1024, 15 * 32768, 0, 0, 8 * per)):
+        d = D.make_desc(1, 64, 8, 128, lq, lk, qs, ks, window=win)
+        assert D.dfa_attn_workspace_size(d, D.DFA_OP_BWD) == want, (lq, lk, win)
+    band = D.make_desc(1, 64, 8, 128, 32768, 32768, 15 * 32768, 14 * 32768, window=4096)
+    n = D.dfa_attn_workspace_size(band, D.DFA_OP_BWD)
+    assert n > 0 and n % (2 * 32768 * 8 * 128 * 4) == 0 and n <= 4 << 30
+    assert D.dfa_attn_workspace_size(D.make_desc(1, 2, 2, 64, 4096, 64, dtype="f32"),
+                                     D.DFA_OP_BWD) == 0
+
+
+def test_workspace_size_errors(dfa_lib):
     L = dfa_lib.lib()
-    assert L.dfa_test_mfma_loop(0, 2, 0, FAKE, None) == D.DFA_ERR_INVALID      # no workgroups
-    assert L.dfa_test_mfma_loop(4, 3, 0, FAKE, None) == D.DFA_ERR_INVALID      # odd iters
-    assert L.dfa_test_mfma_loop(4, 2, 1, None, None) == D.DFA_ERR_INVALID      # no sink
-    assert L.dfa_test_mfma_loop(4, 2, 4, FAKE, None) == D.DFA_ERR_INVALID      # unknown mode
-    assert dfa_lib.dfa_last_error().startswith("dfa_test_mfma_loop")
+    d = D.make_desc(1, 4, 2, 128, 256, 256)
+    n = ctypes.c_int64(0)
+    assert L.dfa_attn_workspace_size(ctypes.byref(d), 2, ctypes.byref(n)) == D.DFA_ERR_INVALID
+    assert L.dfa_attn_workspace_size(ctypes.byref(d), 0, None) == D.DFA_ERR_INVALID
+    assert L.dfa_attn_workspace_size(None, 0, ctypes.byref(n)) == D.DFA_ERR_INVALID
+    d.head_dim = 96
+    assert L.dfa_attn_workspace_size(ctypes.byref(d), 0, ctypes.byref(n)) == D.DFA_ERR_UNSUPPORTED
+
+
+def test_undersized_workspace_is_a_capacity_error(dfa_lib):
+    """A workspace smaller than the query's answer (or none) fails with
+    DFA_ERR_CAPACITY naming the required size, before anything is enqueued
+    (the pointers are fake; no GPU is touched)."""
+    L = dfa_lib.lib()
+    d = D.make_desc(1, 4, 2, 128, 256, 300)
+    need = dfa_lib.dfa_attn_workspace_size(d, D.DFA_OP_FWD)
+    assert need == 2 * 2 * 128 * 384
+    assert _fwd(L, d) == D.DFA_ERR_CAPACITY                       # no workspace
+    assert f"{need} bytes required" in dfa_lib.dfa_last_error()
+    d.workspace, d.workspace_bytes = 1 << 24, need - 1
+    assert _fwd(L, d) == D.DFA_ERR_CAPACITY
+    assert f"{need - 1} given" in dfa_lib.dfa_last_error()
+    d.workspace, d.workspace_bytes = (1 << 24) + 8, need
+    assert _fwd(L, d) == D.DFA_ERR_INVALID                        # misaligned workspace
+    assert "aligned" in dfa_lib.dfa_last_error()
+    g = D.make_desc(1, 64, 8, 128, 32768, 1024, 15 * 32768, 0)   # splits: needs scratch
+    need_b = dfa_lib.dfa_attn_workspace_size(g, D.DFA_OP_BWD)
+    g.workspace, g.workspace_bytes = 1 << 24, need_b - 16
+
+    def bwd(desc):
+        return L.dfa_attn_bwd(ctypes.byref(desc), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1,
+                              FAKE, FAKE, FAKE, None)
+
+    assert bwd(g) == D.DFA_ERR_CAPACITY
+    assert f"{need_b} bytes required" in dfa_lib.dfa_last_error()
+
+
+def test_bwd_without_keys_still_computes_delta(dfa_lib):
+    """A pair with no keys adds nothing to dq, dk, dv, but with
+    compute_delta = 1 it still writes delta, which later pairs of the query
+    chunk read: without a GPU the delta launch is attempted (DFA_ERR_HIP),
+    and with compute_delta = 0 the call returns at once."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present (the GPU tests cover this case)")
+    L = dfa_lib.lib()
+    d = D.make_desc(1, 2, 2, 64, 64, 0)
+
+    def bwd(cd):
+        return L.dfa_attn_bwd(ctypes.byref(d), None, None, None, FAKE, None, FAKE, FAKE, cd,
+                              None, None, None, None)
+
+    assert bwd(0) == D.DFA_OK
+    assert bwd(1) == D.DFA_ERR_HIP
+
+
+def test_chunk_transfer_argument_errors(dfa_lib):
+    """The emulated exchange copy checks its arguments before the runtime:
+    negative sizes, null pointers and overlapping ranges are rejected, and a
+    zero-byte transfer enqueues nothing."""
+    L = dfa_lib.lib()
+    a, b = ctypes.c_void_p(1 << 24), ctypes.c_void_p((1 << 24) + 4096)
+    assert L.dfa_chunk_transfer(a, b, -1, None) == D.DFA_ERR_INVALID
+    assert L.dfa_chunk_transfer(None, b, 16, None) == D.DFA_ERR_INVALID
+    assert L.dfa_chunk_transfer(a, None, 16, None) == D.DFA_ERR_INVALID
+    assert L.dfa_chunk_transfer(a, b, 4097, None) == D.DFA_ERR_INVALID    # ranges overlap
+    assert "overlap" in dfa_lib.dfa_last_error()
+    assert L.dfa_chunk_transfer(b, a, 4097, None) == D.DFA_ERR_INVALID
+    assert L.dfa_chunk_transfer(None, None, 0, None) == D.DFA_OK

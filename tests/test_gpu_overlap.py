@@ -1,15 +1,16 @@
 """The two-stream exchange emulation ([DistFlashAttn §3.2]: key/value
-prefetch on a separate stream, overlapped with compute) gives bitwise the
-results of the plain forward, for owners and for helpers whose results are
-sent back to their owners."""
+prefetch on a separate stream, overlapped with compute) gives the oracle's
+partials, and bitwise the results of the plain forward, for owners and for
+helpers whose results are sent back to their owners."""
 
 import numpy as np
 import pytest
 import torch
 
+import oracle
 from long_context_exact_amd.runner import ChunkedCausalAttention
 
-from _util import rand, to_dev
+from _util import check_lse, check_o, rand, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -25,9 +26,10 @@ def test_overlapped_worker_forward_is_bitwise_plain(p, c, window):
     print(f"case overlap {p} {c} {window}", flush=True)
     rng = np.random.default_rng(p * 10 + c)
     att = ChunkedCausalAttention(p, c, 1, 4, 2, 128, "bf16", window=window)
-    q = {a: to_dev(rand(rng, att.q_shape(), "bf16"), "bf16") for a in range(p)}
-    k = {a: to_dev(rand(rng, att.kv_shape(), "bf16"), "bf16") for a in range(p)}
-    v = {a: to_dev(rand(rng, att.kv_shape(), "bf16"), "bf16") for a in range(p)}
+    qh = [rand(rng, att.q_shape(), "bf16") for _ in range(p)]
+    kh = [rand(rng, att.kv_shape(), "bf16") for _ in range(p)]
+    vh = [rand(rng, att.kv_shape(), "bf16") for _ in range(p)]
+    q, k, v = ({a: to_dev(x[a], "bf16") for a in range(p)} for x in (qh, kh, vh))
     ref = {(it[2], it[3]): att.new_partial() for it in att.items}
     att.forward_items(att.items, q, k, v, ref)
     for overlap in (True, False):
@@ -38,3 +40,8 @@ def test_overlapped_worker_forward_is_bitwise_plain(p, c, window):
         for key in ref:
             assert torch.equal(got[key][0], ref[key][0]), (overlap, key)
             assert torch.equal(got[key][1], ref[key][1]), (overlap, key)
+            a, cc = key
+            ro, rl = oracle.attention_fwd(qh[a], kh[cc], vh[cc], att.scale, True, a * c, cc * c,
+                                          window=window)
+            check_o(to_np(got[key][0]), ro, "bf16", f"overlapped O_part{key}")
+            check_lse(to_np(got[key][1]), rl, "bf16", f"overlapped LSE_part{key}")

@@ -284,12 +284,35 @@ def test_backward_accumulates_into_existing_gradients():
     check_lse(to_np(delta), oracle.attention_delta(to_np(o_in), d_o), "f32", "delta")
 
 
-def test_mfma_calibration_loop_runs():
-    """The matrix-core calibration loop runs in all four modes (constant or
-    random operands, accumulators anywhere or in AGPRs) and leaves its sink
-    untouched."""
-    sink = torch.zeros(8 * 256, device=DEV)
-    for mode in range(4):
-        D.dfa_test_mfma_loop(8, 64, mode, sink)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_empty_first_pair_still_writes_delta(dtype):
+    """A query chunk whose first backward call has no keys (len_kv = 0) must
+    still write delta when compute_delta is 1: the next pair, called with
+    compute_delta = 0, reads it.  Compared with the oracle's gradient."""
+    print(f"case empty first pair {dtype}", flush=True)
+    rng = np.random.default_rng(case_seed(("empty-first", dtype)))
+    hq, hkv, dh, lq, lk = 4, 2, 64, 96, 80
+    q, d_o = (rand(rng, (1, lq, hq, dh), dtype) for _ in range(2))
+    k, v = (rand(rng, (1, lk, hkv, dh), dtype) for _ in range(2))
+    scale = dh ** -0.5
+    ro, rl = oracle.attention_fwd(q, k, v, scale, True, 100, 0)
+    o_in = to_dev(bf16_round(ro.astype(np.float32)) if dtype == "bf16" else
+                  ro.astype(np.float32), dtype)
+    lse = torch.from_numpy(rl.astype(np.float32)).to(DEV)
+    delta = torch.full_like(lse, float("nan"))
+    dq = torch.zeros(1, lq, hq, dh, device=DEV)
+    dk = torch.zeros(1, lk, hkv, dh, device=DEV)
+    dv = torch.zeros_like(dk)
+    empty = torch.zeros(1, 0, hkv, dh, device=DEV, dtype=TD[dtype])
+    e32 = torch.zeros(1, 0, hkv, dh, device=DEV)
+    D.dfa_attn_bwd(D.make_desc(1, hq, hkv, dh, lq, 0, 100, 0, dtype=dtype), to_dev(q, dtype),
+                   empty, empty, o_in, lse, to_dev(d_o, dtype), delta, True, dq, e32, e32)
+    D.dfa_attn_bwd(D.make_desc(1, hq, hkv, dh, lq, lk, 100, 0, dtype=dtype), to_dev(q, dtype),
+                   to_dev(k, dtype), to_dev(v, dtype), None, lse, to_dev(d_o, dtype), delta, False,
+                   dq, dk, dv)
     torch.cuda.synchronize()
-    assert torch.all(sink == 0)
+    check_lse(to_np(delta), oracle.attention_delta(to_np(o_in), d_o), "f32", "delta")
+    rq, rk, rv = oracle.attention_bwd(q, k, v, to_np(o_in), rl, d_o, scale, True, 100, 0)
+    check_grad(to_np(dq), rq, dtype, "dQ")
+    check_grad(to_np(dk), rk, dtype, "dK")
+    check_grad(to_np(dv), rv, dtype, "dV")

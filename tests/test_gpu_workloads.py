@@ -8,6 +8,11 @@ any size instead:
   sum_j dK_j = 0 (each row's dS sums to zero),
 plus exact dK/dV rows for sampled keys where the rows that see them fit.
 
+For the worker shares, dK and dV of every key are also compared element
+by element: a second backward with dO zero outside 64 sampled rows makes
+every key's gradient exactly those rows' contribution, which the oracle
+computes from them alone.
+
 Sizes: 32768-token sequence (8 x 4096, forward only), 65536 (8 x 8192,
 forward + backward), and worker 15's query chunk at 16 x 16384 (32 heads)
 and 16 x 32768 (64 query heads over 8 key/value heads)."""
@@ -54,7 +59,7 @@ def _run(w, att, host, owners, items, backward, kv_bufs=None):
     lse = {a: torch.empty(att.lse_shape(), device=DEV) for a in owners}
     for a in owners:
         att.merge_owner(a, partials, o[a], lse[a])
-    res = {"o": o, "lse": lse, "partials": partials}
+    res = {"o": o, "lse": lse, "partials": partials, "dev": dev}
     if backward:
         kvs = kv_bufs if kv_bufs is not None else sorted({it[3] for it in items})
         dq = {a: torch.zeros(att.q_shape(), device=DEV) for a in owners}
@@ -165,6 +170,56 @@ def test_llama7b_64k_forward_backward():
     assert rel_fro(np.concatenate(got_v), np.concatenate(want_v)) <= 2e-2
 
 
+def _check_dkdv_sparse_do(w, att, host, res, a, items, heads, runs):
+    """dK / dV of every key of every key/value chunk, element by element.
+
+    The backward is run again with dO zero except on the sampled query rows
+    (`runs`: (first row, count) of chunk a) of the sampled heads.  Every
+    other row then has delta = <dO, O> = 0 and dP = dO V^T = 0, hence
+    dS = P (dP - delta) = 0, so it adds nothing: each key's dK and dV are
+    exactly the sampled rows' contributions, which the oracle computes from
+    those rows alone (their own full-prefix O and LSE).  The launch
+    configuration is the one the bench times (same pairs, same kernels)."""
+    c, grp, dev = w.chunk, w.heads_q // w.heads_kv, res["dev"]
+    sparse = np.zeros((w.batch, c, w.heads_q, w.head_dim), dtype=np.float32)
+    for h in heads:
+        for r0, n in runs:
+            sparse[:, r0:r0 + n, h] = host[3][a][:, r0:r0 + n, h]
+    d_o = {a: torch.from_numpy(sparse).to(DEV).to(TD[w.dtype])}
+    kvs = sorted({it[3] for it in items})
+    dq = {a: torch.zeros(att.q_shape(), device=DEV)}
+    dk = {j: torch.zeros(att.kv_shape(), device=DEV) for j in kvs}
+    dv = {j: torch.zeros(att.kv_shape(), device=DEV) for j in kvs}
+    delta = {a: torch.empty(att.lse_shape(), device=DEV)}
+    att.backward_items(items, dev[0], dev[1], dev[2], res["o"], res["lse"], d_o, delta, dq, dk, dv)
+    torch.cuda.synchronize()
+    for g in sorted({h // grp for h in heads}):
+        kp, vp = _prefix(host, 1, a, g), _prefix(host, 2, a, g)
+        want_k, want_v = np.zeros_like(kp), np.zeros_like(vp)
+        for h in (x for x in heads if x // grp == g):
+            for r0, n in runs:
+                qr = host[0][a][:, r0:r0 + n, h:h + 1].astype(np.float64)
+                dor = host[3][a][:, r0:r0 + n, h:h + 1].astype(np.float64)
+                ro, rl = oracle.attention_fwd(qr, kp, vp, w.scale, True, a * c + r0, 0)
+                _, rk, rv = oracle.attention_bwd(qr, kp, vp, ro, rl, dor, w.scale, True,
+                                                 a * c + r0, 0)
+                want_k += rk
+                want_v += rv
+        for j in kvs:
+            for name, got_t, want in (("dK", dk, want_k), ("dV", dv, want_v)):
+                got = to_np(got_t[j][:, :, g])
+                ref = want[:, j * c:(j + 1) * c, 0]
+                r = rel_fro(got, ref)
+                m = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
+                print(f"  {name} chunk {j} kv head {g}: rel fro {r:.2e}, max err / max {m:.2e}",
+                      flush=True)
+                assert r <= 2e-2 and m <= 2e-2, (name, j, g, r, m)
+    # the other kv heads saw no sampled row: exactly zero
+    for j in kvs:
+        for g in set(range(w.heads_kv)) - {h // grp for h in heads}:
+            assert torch.all(dk[j][:, :, g] == 0) and torch.all(dv[j][:, :, g] == 0)
+
+
 @pytest.mark.parametrize("name", ["llama7b_256k_w15", "gqa64x8_512k_w15"])
 def test_worker_share_forward_backward(name):
     """Worker 15's query chunk: its own 9 pairs plus the 7 pairs helpers
@@ -183,6 +238,13 @@ def test_worker_share_forward_backward(name):
     c = w.chunk
     _check_rows(w, host, res, a, [0, 1, c // 2, c - 1], [0, w.heads_q - 1], True)
     _check_grad_identities(w, host, res, [a], kvs)
+    # 64 rows in four runs of 16 (the first rows, two runs off the 32-row
+    # tile grid, and the last rows at the diagonal's causal edge), in query
+    # heads of at least two key/value groups
+    grp = w.heads_q // w.heads_kv
+    heads = [0, 1, grp + 1, w.heads_q - 1] if grp > 1 else [0, w.heads_q - 1]
+    runs = [(0, 16), (c // 3 + 5, 16), (2 * c // 3 + 11, 16), (c - 16, 16)]
+    _check_dkdv_sparse_do(w, att, host, res, a, items, heads, runs)
 
 
 def test_windowed_worker_share_forward_backward():
