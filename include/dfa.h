@@ -38,7 +38,8 @@
  * they work on a machine without a GPU.
  *
  * Thread safety: the library keeps no state between calls (apart from the
- * calling thread's last error message) and every call may be made from any
+ * calling thread's last error message, and the per-device scratch of
+ * dfa_attn_fwd_partial_noalloc) and every call may be made from any
  * thread.  A call may enqueue several kernels that pass data through its
  * workspace, so calls that share one workspace must be ordered: issued by
  * one thread on one stream, or on streams ordered with events.  Calls with
@@ -191,6 +192,23 @@ dfa_status dfa_global_window_schedule(int32_t num_workers, int64_t chunk_len,
 dfa_status dfa_attn_fwd_partial(const dfa_attn_desc* desc, const void* q,
                                 const void* k, const void* v, float* o_part,
                                 float* lse, void* hip_stream);
+
+/* The forward of dfa_attn_fwd_partial for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernels and results, but the
+ * transposed V lives in a fixed array of the library's own device memory
+ * (64 MiB per device, loaded with the library's code, kept until the
+ * process ends; its address is resolved on the first call on each device)
+ * and desc->workspace is ignored.  The call allocates and frees nothing.
+ * A pair whose transposed V exceeds 64 MiB (dfa_attn_workspace_size,
+ * DFA_OP_FWD) returns DFA_ERR_CAPACITY.  Every call on a device shares that
+ * device's array: calls that overlap on one device (different streams, or
+ * host threads interleaving on one stream) race; the array needs no
+ * clearing (each call writes all of the part it reads). */
+dfa_status dfa_attn_fwd_partial_noalloc(const dfa_attn_desc* desc,
+                                        const void* q, const void* k,
+                                        const void* v, float* o_part,
+                                        float* lse, void* hip_stream);
 
 /* LSE merge of n partial states of the same query rows over disjoint key
  * sets ([DistFlashAttn §3.2, Fig. 3]: the owner rescales the partials it

@@ -30,7 +30,7 @@ _TORCH = {DFA_F32: torch.float32, DFA_BF16: torch.bfloat16}
 EXPORTED = (
     "dfa_balanced_schedule", "dfa_window_schedule", "dfa_global_window_schedule",
     "dfa_attn_fwd_partial", "dfa_lse_merge", "dfa_attn_bwd", "dfa_attn_workspace_size",
-    "dfa_chunk_transfer",
+    "dfa_chunk_transfer", "dfa_attn_fwd_partial_noalloc",
     "dfa_last_error", "dfa_version", "dfa_test_tile_shape", "dfa_test_fwd_tile_visits",
     "dfa_test_bwd_part",
 )
@@ -97,9 +97,10 @@ def lib() -> ctypes.CDLL:
                                         P]
         L.dfa_attn_workspace_size.argtypes = [ctypes.POINTER(AttnDesc), I32, ctypes.POINTER(I64)]
         L.dfa_chunk_transfer.argtypes = [P, P, I64, P]
+        L.dfa_attn_fwd_partial_noalloc.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P]
         for name in ("dfa_balanced_schedule", "dfa_window_schedule", "dfa_global_window_schedule",
                      "dfa_attn_fwd_partial", "dfa_lse_merge", "dfa_attn_workspace_size",
-                     "dfa_chunk_transfer",
+                     "dfa_chunk_transfer", "dfa_attn_fwd_partial_noalloc",
                      "dfa_attn_bwd", "dfa_test_tile_shape", "dfa_test_fwd_tile_visits",
                      "dfa_test_bwd_part"):
             getattr(L, name).restype = I32
@@ -252,6 +253,16 @@ def dfa_attn_fwd_partial(desc: AttnDesc, q, k, v, o_part, lse, stream=None, work
             _ptr(o_part, "o_part", qs, torch.float32), _ptr(lse, "lse", ls, torch.float32))
     d, _keep = _with_workspace(desc, DFA_OP_FWD, workspace, stream)
     _check(lib().dfa_attn_fwd_partial(ctypes.byref(d), *args, _stream(stream)))
+
+
+def dfa_attn_fwd_partial_noalloc(desc: AttnDesc, q, k, v, o_part, lse, stream=None):
+    """dfa_attn_fwd_partial with its scratch in the library's fixed per-device
+    array: allocates nothing (for code that cannot allocate)."""
+    qs, ks, ls = _shapes(desc)
+    dt = _TORCH.get(desc.dtype, torch.bfloat16)
+    args = (_ptr(q, "q", qs, dt), _ptr(k, "k", ks, dt), _ptr(v, "v", ks, dt),
+            _ptr(o_part, "o_part", qs, torch.float32), _ptr(lse, "lse", ls, torch.float32))
+    _check(lib().dfa_attn_fwd_partial_noalloc(ctypes.byref(desc), *args, _stream(stream)))
 
 
 def dfa_lse_merge(o_parts: Sequence[torch.Tensor], lse_parts: Sequence[torch.Tensor], batch: int,
