@@ -331,25 +331,36 @@ def main():
         return call
 
     pairs_x_heads = n_pairs * w.batch * w.heads_q
-    # name in the profiler, time per step, flop per step (the kernel's own
-    # contractions on unmasked pairs: forward 2 = 4d, dK/dV 4 = 8d, dQ 3 = 6d)
+    # name in the profiler -> (time per step, algorithmic FLOP per step,
+    # executed MFMA FLOP per step).  Algorithmic: each kernel's share of the
+    # method's work, so that the shares sum to the 14d per visible pair the
+    # step counts (forward 4d: S, PV; dK/dV 8d: S, dP, dV, dK; dQ 2d: the dQ
+    # product; its S and dP repeat the dK/dV kernel's and are executed work
+    # only, 4d more).
     names = KERNEL_NAMES if w.dtype == "bf16" else KERNEL_NAMES_F32
-    kernels = {names["fwd"]: (per_call(fwd_call, timed), pairs_x_heads * 4 * w.head_dim)}
+    kernels = {names["fwd"]: (per_call(fwd_call, timed), pairs_x_heads * 4 * w.head_dim,
+                              pairs_x_heads * 4 * w.head_dim)}
     if w.backward:
-        kernels[names["dkdv"]] = (per_call(bwd_call(1), timed),
-                                         pairs_x_heads * 8 * w.head_dim)
-        kernels[names["dq"]] = (per_call(bwd_call(2), timed),
-                                       pairs_x_heads * 6 * w.head_dim)
+        kernels[names["dkdv"]] = (per_call(bwd_call(1), timed), pairs_x_heads * 8 * w.head_dim,
+                                  pairs_x_heads * 8 * w.head_dim)
+        kernels[names["dq"]] = (per_call(bwd_call(2), timed), pairs_x_heads * 2 * w.head_dim,
+                                pairs_x_heads * 6 * w.head_dim)
     nl = len(timed)
-    name, (kms, kflop) = max(kernels.items(), key=lambda kv: kv[1][0])
+    name, (kms, kflop, _) = max(kernels.items(), key=lambda kv: kv[1][0])
     achieved = kflop / (kms * 1e-3) / 1e12
+    tf = lambda f, ms: round(f / (ms * 1e-3) / 1e12, 2)  # noqa: E731
     roofline = {"bound": "mfma" if w.dtype == "bf16" else "alu", "kernel": name, "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": traffic_of(name, nl, w.name), "avg_launch_ms": round(kms / nl, 3),
                 "launches_per_step": nl, "flop_per_launch": kflop / nl,
                 "others": {n: {"avg_launch_ms": round(x[0] / nl, 3),
-                               "tflops": round(x[1] / (x[0] * 1e-3) / 1e12, 2)}
+                               "tflops": tf(x[1], x[0]), "executed_tflops": tf(x[2], x[0])}
                            for n, x in kernels.items()}}
+    if w.backward:
+        bms = kernels[names["dkdv"]][0] + kernels[names["dq"]][0]
+        roofline["backward_pair"] = {"avg_launch_ms": round(bms / nl, 3),
+                                     "tflops": tf(pairs_x_heads * 10 * w.head_dim, bms),
+                                     "executed_tflops": tf(pairs_x_heads * 14 * w.head_dim, bms)}
 
     result = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,

@@ -35,10 +35,11 @@ COMMON_FLAGS = [
 ]
 
 
-# Per-source compiler options, each measured on its kernel: the forward
-# schedules best with the ILP-maximising machine scheduler (about 2.5 %
-# faster), dQ with the AMDGPU register-pressure trackers (about 6 %).
+# Per-source compiler options, each measured on its kernel: the forward and
+# dK/dV schedule best with the ILP-maximising machine scheduler (about 2.5 %
+# and 1 % faster), dQ with the AMDGPU register-pressure trackers (about 6 %).
 FILE_FLAGS = {"fwd_mfma.hip": ["-mllvm", "--amdgpu-sched-strategy=max-ilp"],
+              "dkdv_mfma.hip": ["-mllvm", "--amdgpu-sched-strategy=max-ilp"],
               "dq_mfma.hip": ["-mllvm", "--amdgpu-use-amdgpu-trackers"]}
 
 

@@ -188,6 +188,27 @@ void dkdv_bf16_kernel(BwdArgs a) {
 #pragma unroll
       for (int st = 0; st < D / 16; ++st)
         dp = mfma32(tile_row8<D>(dOs, l32, 2 * st + hi), tile_row8<D>(Vs, wave * 32 + l32, 2 * st + hi), dp);
+      if constexpr (FULL && D == 128) {
+        // Schedule of the 16 products above: each operand's LDS read is
+        // issued three products ahead of the product that takes it (left to
+        // itself, at this register budget, the scheduler issues each read
+        // just before its product, and the product then waits out the LDS
+        // latency).  Groups in order: 3 Q reads; S0..S4 each followed by
+        // the next Q read; S5..S7 each followed by one dO and one V read;
+        // dP0..dP4 likewise; dP5..dP7.
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // 0x100: LDS reads
+#pragma unroll
+        for (int k = 0; k < 5; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 0x008: MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+      }
       bool need_mask = false;
       if constexpr (!FULL)
         need_mask = (a.causal && a.q_start + r0 < a.kv_start + wk_hi - 1) ||

@@ -107,6 +107,19 @@ void dq_bf16_kernel(BwdArgs a) {
       s = mfma32(tile_row8<D>(Ks, kb * 32 + l32, 2 * st + hi), qf[st], s);
       dp = mfma32(tile_row8<D>(Vs, kb * 32 + l32, 2 * st + hi), df[st], dp);
     }
+    if constexpr (FULL && D == 128) {
+      // Each operand's LDS read three products ahead of the product that
+      // takes it (0x100: LDS reads, 0x008: MFMA); left to itself, at this
+      // register budget, the scheduler issues each read just before its
+      // product, which then waits out the LDS latency.
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+      for (int k = 0; k < 13; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+    }
   };
   // dS^T = P^T (dP^T - delta) (hidden scores already -inf), dQ^T += K^T dS^T.
   auto update = [&](const lds_u16* Ks, int kb, const f32x16& s, f32x16& dp) {

@@ -151,6 +151,18 @@ void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
     for (int st = 0; st < D / 16; ++st)
       s = mfma32(tile_row8<D>(Ks, kb * 32 + l32, 2 * st + hi), qf[st], s);
+    if constexpr (FULL && D == 128) {
+      // Each K read three products ahead of the product that takes it
+      // (0x100: LDS reads, 0x008: MFMA); left to itself, at this register
+      // budget, the scheduler issues each read just before its product.
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+      for (int k = 0; k < 5; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+    }
     return s;
   };
   // Online-softmax update with the sub-block's scores (hidden ones -inf);
