@@ -188,7 +188,7 @@ void dkdv_bf16_kernel(BwdArgs a) {
 #pragma unroll
       for (int st = 0; st < D / 16; ++st)
         dp = mfma32(tile_row8<D>(dOs, l32, 2 * st + hi), tile_row8<D>(Vs, wave * 32 + l32, 2 * st + hi), dp);
-      if constexpr (FULL && D == 128) {
+      if constexpr (D == 128) {
         // Schedule of the 16 products above: each operand's LDS read is
         // issued three products ahead of the product that takes it (left to
         // itself, at this register budget, the scheduler issues each read

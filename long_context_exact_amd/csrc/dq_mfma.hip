@@ -107,7 +107,7 @@ void dq_bf16_kernel(BwdArgs a) {
       s = mfma32(tile_row8<D>(Ks, kb * 32 + l32, 2 * st + hi), qf[st], s);
       dp = mfma32(tile_row8<D>(Vs, kb * 32 + l32, 2 * st + hi), df[st], dp);
     }
-    if constexpr (FULL && D == 128) {
+    if constexpr (D == 128) {
       // Each operand's LDS read three products ahead of the product that
       // takes it (0x100: LDS reads, 0x008: MFMA); left to itself, at this
       // register budget, the scheduler issues each read just before its

@@ -151,7 +151,7 @@ void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
     for (int st = 0; st < D / 16; ++st)
       s = mfma32(tile_row8<D>(Ks, kb * 32 + l32, 2 * st + hi), qf[st], s);
-    if constexpr (FULL && D == 128) {
+    if constexpr (D == 128) {
       // Each K read three products ahead of the product that takes it
       // (0x100: LDS reads, 0x008: MFMA); left to itself, at this register
       // budget, the scheduler issues each read just before its product.
