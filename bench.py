@@ -59,7 +59,8 @@ def source_digest(name: str) -> str:
 
 
 def traffic_of(name: str, launches: int, workload: str):
-    """HBM bytes per launch of `name` from the committed counter summary, or
+    """HBM bytes per launch of `name` from the committed counter summary (the
+    total, the FETCH and WRITE parts and what they were averaged over), or
     None if there is none, it was taken on another workload, or the kernel's
     sources changed since it was taken."""
     try:
@@ -349,9 +350,11 @@ def main():
     name, (kms, kflop, _) = max(kernels.items(), key=lambda kv: kv[1][0])
     achieved = kflop / (kms * 1e-3) / 1e12
     tf = lambda f, ms: round(f / (ms * 1e-3) / 1e12, 2)  # noqa: E731
+    tdetail = traffic_of(name, nl, w.name)
     roofline = {"bound": "mfma" if w.dtype == "bf16" else "alu", "kernel": name, "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": traffic_of(name, nl, w.name), "avg_launch_ms": round(kms / nl, 3),
+                "traffic": None if tdetail is None else tdetail["bytes_per_launch"],
+                "traffic_detail": tdetail, "avg_launch_ms": round(kms / nl, 3),
                 "launches_per_step": nl, "flop_per_launch": kflop / nl,
                 "others": {n: {"avg_launch_ms": round(x[0] / nl, 3),
                                "tflops": tf(x[1], x[0]), "executed_tflops": tf(x[2], x[0])}
