@@ -180,8 +180,8 @@ dfa_status dfa_global_window_schedule(int32_t num_workers, int64_t chunk_len,
                                       int64_t* num_items, int32_t* num_steps);
 
 /* Partial attention of one chunk pair: the normalised output and its LSE
- * ([DistFlashAttn App. D]: the forward returns output and logsumexp values;
- * §3.2: partial outputs and softmax statistics are what a helper returns).
+ * ([DistFlashAttn App. D]: per pair the forward hands back the output with
+ * its log-sum-exp; §3.2: a helper sends exactly this state to the owner).
  *   q [B,len_q,Hq,d], k and v [B,len_kv,Hkv,d] in desc->dtype;
  *   o_part [B,len_q,Hq,d] float32 and lse [B,Hq,len_q] float32 are
  *   overwritten.  Only the causal prefix is computed: key tiles entirely

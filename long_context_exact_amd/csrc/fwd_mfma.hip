@@ -1,8 +1,8 @@
 // Forward partial attention of one chunk pair on gfx950 bf16 MFMA.
 //
 // Per chunk pair the kernel returns the normalised output and its natural
-// log-sum-exp ([DistFlashAttn App. D]: the forward returns output and
-// logsumexp values), computing only the causal prefix (§2, §3.2).  Inside
+// log-sum-exp (the per-pair state of [DistFlashAttn App. D]), computing
+// only the causal prefix (§2, §3.2).  Inside
 // the kernel the softmax is the online (running max / running sum) form the
 // paper builds on (FlashAttention, cited prior art), in base 2 with
 // log2(e) folded into the scale.

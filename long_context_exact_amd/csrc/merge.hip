@@ -1,8 +1,8 @@
 // HBM-bound helpers of the hot path: the LSE merge of partial states, the
 // backward preprocess delta = rowsum(dO * O), and the empty-pair fill.
 //
-// LSE merge ([DistFlashAttn §3.2, Fig. 3]: the owner rescales and combines
-// the partial outputs and softmax statistics it receives):
+// LSE merge ([DistFlashAttn §3.2, Fig. 3]: the owner rescales and sums the
+// per-pair outputs its helpers send back, each with its log-sum-exp):
 //   M = max_r LSE_r, LSE = M + ln sum_r exp(LSE_r - M),
 //   O = sum_r exp(LSE_r - LSE) O_r          (ascending r, fp32).
 // One thread owns 4 consecutive head_dim elements of one (row, head); the

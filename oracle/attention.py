@@ -1,8 +1,8 @@
 """Exact causal softmax attention in float64 — TEST INFRASTRUCTURE ONLY.
 
-The paper computes *exact* attention (abstract; §F "the paper focuses on
-exact attention") and its rematerialisation-aware checkpointing changes no
-numbers (§1, §2 "without numerical differences").  So the oracle is the
+The paper computes *exact* attention (abstract; App. F names exact attention
+as its scope) and its rematerialisation-aware checkpointing leaves every
+number unchanged (§1, §2).  So the oracle is the
 plain definition written out: every query row takes one full softmax over
 all of its visible keys at once.  There is no online rescaling, no tiling
 and no chunk merge in ``attention_fwd``; query rows are walked in blocks only
@@ -64,8 +64,8 @@ def _check_window(causal: bool, window: int, n_global: int = 0):
 def _visible(rows: np.ndarray, lk: int, q0: int, k0: int, causal: bool, window: int = 0,
              n_global: int = 0):
     """Boolean [len(rows), lk]: key j visible to query i (global positions,
-    inclusive diagonal: a query sees itself and every earlier token, §3.2
-    "each worker processes only its causal prefix").  window > 0 keeps only
+    inclusive diagonal: a query sees itself and every earlier token; §3.2:
+    a worker attends over the prefix up to its own chunk and nothing later).  window > 0 keeps only
     the keys less than `window` positions behind the query: the local
     sliding window of [App. F], which lets a worker skip non-local keys.
     n_global = G > 0 adds back the global tokens of App. F's global
@@ -86,9 +86,9 @@ def attention_fwd(q, k, v, scale, causal=True, q_start=0, kv_start=0, window=0, 
     block, or for a whole sequence (q_start = kv_start = 0).
 
     The partial state a worker returns for a chunk pair is the normalised
-    output plus its log-sum-exp ([DistFlashAttn App. D]: the forward
-    "returns output and logsumexp values"; §3.2: helpers send back "partial
-    outputs and softmax statistics").
+    output plus its log-sum-exp ([DistFlashAttn App. D]: per pair the
+    forward produces the output together with its log-sum-exp; §3.2: a helper
+    sends that state back to the owner, which rescales and combines it).
 
     Returns (o [B,Lq,Hq,d] float64, lse [B,Hq,Lq] float64).  Rows that see
     no key get o = 0 and lse = -inf.  window > 0 (causal only): the local

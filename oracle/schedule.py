@@ -9,8 +9,8 @@ Unbalanced schedule ([DistFlashAttn §3.2]; App. B, Fig. 5): at step t,
 worker w >= t computes its own queries against chunk w - t, the others
 idle.  P steps; about half the workers idle.
 
-Load-balanced schedule ([DistFlashAttn §1 "token-level workload
-balancing", §3.2 and Fig. 3; App. B, Fig. 6]).  The figure itself is not in
+Load-balanced schedule ([DistFlashAttn §1, its token-level balancing;
+§3.2 and Fig. 3; App. B, Fig. 6]).  The figure itself is not in
 the text, so the assignment is the plainest one that the stated facts fix:
   * step 0: every worker does its diagonal pair (w, w);
   * step t = 1 .. floor(P/2): worker w >= t does (w, w - t) for itself;
