@@ -30,13 +30,18 @@ struct BwdArgs {
   // rsplit = 1 adds straight into dk, dv.
   int32_t rsplit;
   float* ws;
+  // dK/dV row band: of each key block's row tiles (its span below, from its
+  // first visible row), only tiles [band_lo, band_hi) run in this launch, so
+  // that one pair can run as bands of different kernels (0, INT32_MAX: all).
+  int32_t band_lo, band_hi;
 };
 
 // The query-row steps of the dK/dV workgroup owning keys [k_lo, k_lo + bk):
 // rows from the first one at or after its first key to the last one whose
-// window still reaches its last key, in blocks of bq rows, times the
-// group's query heads.  Shared by the launcher, the kernel and the split
-// reduction, so all three agree on which slices exist.
+// window still reaches its last key, in blocks of bq rows (cut to the
+// launch's row band), times the group's query heads.  Shared by the
+// launcher, the kernel and the split reduction, so all three agree on which
+// slices exist.
 struct DkvSpan {
   int qt0, nq, steps;
 };
@@ -49,7 +54,10 @@ __host__ __device__ inline DkvSpan dkdv_span(const BwdArgs& a, int64_t k_lo, int
   if (i_begin >= i_end) return {0, 0, 0};
   const int qt0 = int(i_begin / bq);
   const int nq = int((i_end + bq - 1) / bq) - qt0;
-  return {qt0, nq, a.group * nq};
+  const int lo = a.band_lo < nq ? a.band_lo : nq;
+  const int hi = a.band_hi < nq ? a.band_hi : nq;
+  if (lo >= hi) return {0, 0, 0};
+  return {qt0 + lo, hi - lo, a.group * (hi - lo)};
 }
 
 // LSE in base 2 for the exp2 form; a row without keys (LSE = -inf) gets +inf

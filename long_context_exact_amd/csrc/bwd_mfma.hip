@@ -23,6 +23,7 @@
 // next to the current block's vector work).
 #include <algorithm>
 #include <cfloat>
+#include <climits>
 
 #include "bwd_common.hpp"
 
@@ -50,6 +51,8 @@ BwdArgs bwd_args_of(const dfa_attn_desc& d) {
   a.win = d.window > 0 ? d.window : kNoWindow;
   a.rsplit = 1;  // the dK/dV launcher may split rows
   a.ws = nullptr;
+  a.band_lo = 0;  // and may run a pair as row bands
+  a.band_hi = INT32_MAX;
   return a;
 }
 

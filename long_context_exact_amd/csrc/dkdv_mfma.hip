@@ -2,6 +2,7 @@
 // backward; see bwd_mfma.hip for the pair of kernels and their contract).
 #include <algorithm>
 #include <cfloat>
+#include <climits>
 
 #include "bwd_common.hpp"
 
@@ -378,6 +379,9 @@ int dkdv_row_split(const dfa_attn_desc& d) {
 }
 
 template <int D>
+dfa_status rsplit_reduce(const dfa_attn_desc& d, const BwdArgs& a, hipStream_t s, dfa_status st);
+
+template <int D>
 dfa_status launch_dkdv(const dfa_attn_desc& d, BwdArgs a, hipStream_t s) {
   using C = DkvCfg<D, kDkvNW>;
   const int64_t nkb = cdiv(d.len_kv, C::BK);
@@ -386,17 +390,54 @@ dfa_status launch_dkdv(const dfa_attn_desc& d, BwdArgs a, hipStream_t s) {
   a.rsplit = dkdv_row_split<D>(d);
   a.ws = a.rsplit > 1 ? static_cast<float*>(d.workspace) : nullptr;
   dim3 grid(unsigned(nkb) * unsigned(d.heads_kv), unsigned(d.batch), unsigned(a.rsplit));
-  auto go = [&](auto kern) {
+  auto go = [&](auto kern, const BwdArgs& args) {
     const dfa_status st = allow_lds(kern, C::LDS_BYTES, "dkdv_bf16_kernel");
     if (st != DFA_OK) return st;
-    hipLaunchKernelGGL(kern, grid, dim3(C::NT), C::LDS_BYTES, s, a);
+    hipLaunchKernelGGL(kern, grid, dim3(C::NT), C::LDS_BYTES, s, args);
     return check_launch("dkdv_bf16_kernel");
   };
   // a fully visible pair's key blocks all run the same rows: tile-major order
-  const dfa_status st = (pair_is_full(d, C::BK) && d.len_q % C::BQ == 0)
-                            ? go(dkdv_bf16_kernel<D, kDkvNW, true, true>)
-                        : d.window <= 0 ? go(dkdv_bf16_kernel<D, kDkvNW, false, true>)
-                                        : go(dkdv_bf16_kernel<D, kDkvNW, false, false>);
+  if (pair_is_full(d, C::BK) && d.len_q % C::BQ == 0)
+    return rsplit_reduce<D>(d, a, s, go(dkdv_bf16_kernel<D, kDkvNW, true, true>, a));
+  const bool tm = d.window <= 0;
+  // A diagonal pair (query and key chunk the same tokens) of whole key
+  // blocks runs as row bands: each key block's first BK/BQ row tiles (its
+  // own rows, where the causal edge crosses it) and, with a window, the
+  // tiles from W rows past its first key on (where the window edge crosses
+  // it) in the masked kernel; the rows in between, which see every key of
+  // the block, in the mask-free one.  The bands add into dk, dv one after
+  // the other, so the result stays deterministic.
+  const int own = C::BK / C::BQ;
+  const bool banded = a.rsplit == 1 && d.causal && d.q_start == d.kv_start &&
+                      d.len_q == d.len_kv && d.len_kv % C::BK == 0 &&
+                      (d.window <= 0 || (d.window % C::BQ == 0 && d.window >= 2 * C::BK));
+  if (banded) {
+    const int wt = d.window > 0 ? int(std::min<int64_t>(d.window / C::BQ, INT32_MAX)) : INT32_MAX;
+    BwdArgs band = a;
+    band.band_lo = 0;
+    band.band_hi = own;
+    dfa_status st = tm ? go(dkdv_bf16_kernel<D, kDkvNW, false, true>, band)
+                       : go(dkdv_bf16_kernel<D, kDkvNW, false, false>, band);
+    if (st != DFA_OK) return st;
+    band.band_lo = own;
+    band.band_hi = wt;
+    st = tm ? go(dkdv_bf16_kernel<D, kDkvNW, true, true>, band)
+            : go(dkdv_bf16_kernel<D, kDkvNW, true, false>, band);
+    if (st != DFA_OK || d.window <= 0 || d.window >= d.len_q) return st;
+    band.band_lo = wt;
+    band.band_hi = INT32_MAX;
+    return go(dkdv_bf16_kernel<D, kDkvNW, false, false>, band);
+  }
+  return rsplit_reduce<D>(d, a, s,
+                          tm ? go(dkdv_bf16_kernel<D, kDkvNW, false, true>, a)
+                             : go(dkdv_bf16_kernel<D, kDkvNW, false, false>, a));
+}
+
+// After a launch that split rows (a.rsplit > 1), the fixed-order reduction of
+// its slices into dk, dv.
+template <int D>
+dfa_status rsplit_reduce(const dfa_attn_desc& d, const BwdArgs& a, hipStream_t s, dfa_status st) {
+  using C = DkvCfg<D, kDkvNW>;
   if (st != DFA_OK || a.rsplit == 1) return st;
   const int64_t n4 = int64_t(d.batch) * d.len_kv * d.heads_kv * D / 4;
   hipLaunchKernelGGL((dkdv_split_reduce_kernel<C::BK, C::BQ>), dim3(unsigned(cdiv(n4, 256))),
