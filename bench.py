@@ -339,29 +339,35 @@ def main():
     # product; its S and dP repeat the dK/dV kernel's and are executed work
     # only, 4d more).
     names = KERNEL_NAMES if w.dtype == "bf16" else KERNEL_NAMES_F32
+    calls = [d for it in timed for d, *_ in att.calls(it[2], it[3])]
+    # Kernel launches per step: one forward kernel per call; the dK/dV kernel
+    # runs a diagonal pair of whole key blocks as two or three row-band
+    # launches, so per-launch figures divide by the library's own count.
     kernels = {names["fwd"]: (per_call(fwd_call, timed), pairs_x_heads * 4 * w.head_dim,
-                              pairs_x_heads * 4 * w.head_dim)}
+                              pairs_x_heads * 4 * w.head_dim, len(calls))}
     if w.backward:
         kernels[names["dkdv"]] = (per_call(bwd_call(1), timed), pairs_x_heads * 8 * w.head_dim,
-                                  pairs_x_heads * 8 * w.head_dim)
+                                  pairs_x_heads * 8 * w.head_dim,
+                                  sum(dfa.dfa_test_bwd_launches(d, 1) for d in calls))
         kernels[names["dq"]] = (per_call(bwd_call(2), timed), pairs_x_heads * 2 * w.head_dim,
-                                pairs_x_heads * 6 * w.head_dim)
+                                pairs_x_heads * 6 * w.head_dim,
+                                sum(dfa.dfa_test_bwd_launches(d, 2) for d in calls))
     nl = len(timed)
-    name, (kms, kflop, _) = max(kernels.items(), key=lambda kv: kv[1][0])
+    name, (kms, kflop, _, kl) = max(kernels.items(), key=lambda kv: kv[1][0])
     achieved = kflop / (kms * 1e-3) / 1e12
     tf = lambda f, ms: round(f / (ms * 1e-3) / 1e12, 2)  # noqa: E731
-    tdetail = traffic_of(name, nl, w.name)
+    tdetail = traffic_of(name, kl, w.name)
     roofline = {"bound": "mfma" if w.dtype == "bf16" else "alu", "kernel": name, "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": None if tdetail is None else tdetail["bytes_per_launch"],
-                "traffic_detail": tdetail, "avg_launch_ms": round(kms / nl, 3),
-                "launches_per_step": nl, "flop_per_launch": kflop / nl,
-                "others": {n: {"avg_launch_ms": round(x[0] / nl, 3),
+                "traffic_detail": tdetail, "avg_launch_ms": round(kms / kl, 3),
+                "launches_per_step": kl, "flop_per_launch": kflop / kl,
+                "others": {n: {"avg_launch_ms": round(x[0] / x[3], 3), "launches_per_step": x[3],
                                "tflops": tf(x[1], x[0]), "executed_tflops": tf(x[2], x[0])}
                            for n, x in kernels.items()}}
     if w.backward:
         bms = kernels[names["dkdv"]][0] + kernels[names["dq"]][0]
-        roofline["backward_pair"] = {"avg_launch_ms": round(bms / nl, 3),
+        roofline["backward_pair"] = {"avg_pair_ms": round(bms / nl, 3),
                                      "tflops": tf(pairs_x_heads * 10 * w.head_dim, bms),
                                      "executed_tflops": tf(pairs_x_heads * 14 * w.head_dim, bms)}
 

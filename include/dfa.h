@@ -297,6 +297,15 @@ dfa_status dfa_test_bwd_part(const dfa_attn_desc* desc, const void* q,
                              float* dk, float* dv, int32_t part,
                              void* hip_stream);
 
+/* Kernel launches that dfa_test_bwd_part(desc, ..., part, ...) makes for
+ * its kernel (part 1: the dK/dV kernel, whose diagonal pairs of whole
+ * 256-key blocks run as two or three row-band launches; part 2: the dQ
+ * kernel, one launch), written to *launches; 0 for a pair without query
+ * rows or keys.  Host arithmetic only (no HIP call): a per-launch time is
+ * a call's time divided by this count. */
+dfa_status dfa_test_bwd_launches(const dfa_attn_desc* desc, int32_t part,
+                                 int32_t* launches);
+
 
 #ifdef __cplusplus
 }

@@ -3,6 +3,7 @@
 #include <cstring>
 #include <string>
 
+#include "bwd_common.hpp"
 #include "kernels.hpp"
 
 namespace dfa {
@@ -215,6 +216,22 @@ extern "C" dfa_status dfa_test_bwd_part(const dfa_attn_desc* desc, const void* q
   }
 }
 
+extern "C" dfa_status dfa_test_bwd_launches(const dfa_attn_desc* desc, int32_t part,
+                                            int32_t* launches) {
+  try {
+    DFA_TRY(check_desc("dfa_test_bwd_launches", desc));
+    if (part != 1 && part != 2)
+      return fail(DFA_ERR_INVALID, "dfa_test_bwd_launches: part must be 1 or 2");
+    if (launches == nullptr) return fail(DFA_ERR_INVALID, "dfa_test_bwd_launches: launches is null");
+    const dfa_attn_desc& d = *desc;
+    const bool empty = d.batch == 0 || d.len_q == 0 || d.len_kv == 0;
+    *launches = part == 1 ? dkdv_launches(d) : (empty ? 0 : 1);
+    return DFA_OK;
+  } catch (...) {
+    return fail(DFA_ERR_INVALID, "dfa_test_bwd_launches: internal error");
+  }
+}
+
 extern "C" dfa_status dfa_attn_workspace_size(const dfa_attn_desc* desc, int32_t op,
                                               int64_t* bytes) {
   try {
@@ -232,7 +249,7 @@ extern "C" dfa_status dfa_attn_workspace_size(const dfa_attn_desc* desc, int32_t
   }
 }
 
-extern "C" int32_t dfa_version(void) { return 10000; }
+extern "C" int32_t dfa_version(void) { return 10100; }
 
 extern "C" dfa_status dfa_test_tile_shape(const dfa_attn_desc* desc, int32_t* bm, int32_t* bn) {
   DFA_TRY(check_desc("dfa_test_tile_shape", desc));

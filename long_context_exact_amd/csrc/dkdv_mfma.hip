@@ -381,13 +381,47 @@ int dkdv_row_split(const dfa_attn_desc& d) {
 template <int D>
 dfa_status rsplit_reduce(const dfa_attn_desc& d, const BwdArgs& a, hipStream_t s, dfa_status st);
 
+// How the dK/dV kernel runs a descriptor: its row split, and whether (and
+// where) it runs as row bands.  A diagonal pair (query and key chunk the
+// same tokens) of whole key blocks runs as row bands, each a launch over
+// every key block: the block's own BK/BQ row tiles (where the causal edge
+// crosses it) in the masked kernel, the rows from there to W rows past its
+// first key (every one of which sees all its keys) in the mask-free kernel,
+// and, with a window, the rows from W on (where the window edge crosses it)
+// in the masked kernel again.  The masked kernel's mask branch splits every
+// step's code, so it is kept to the steps that need it; the bands add into
+// dk, dv one after the other, so the result stays deterministic.
+template <int D>
+struct DkvPlan {
+  int rsplit;    // row slices per key block (1: none)
+  bool banded;
+  int own, wt;   // band limits in row tiles: [0, own) masked, [own, wt) mask-free, [wt, ..) masked
+  int launches;  // dK/dV kernel launches (the split reduction not counted)
+};
+
+template <int D>
+DkvPlan<D> dkdv_plan(const dfa_attn_desc& d) {
+  using C = DkvCfg<D, kDkvNW>;
+  DkvPlan<D> p{dkdv_row_split<D>(d), false, 0, INT32_MAX, 1};
+  if (pair_is_full(d, C::BK) && d.len_q % C::BQ == 0) return p;
+  p.banded = p.rsplit == 1 && d.causal && d.q_start == d.kv_start && d.len_q == d.len_kv &&
+             d.len_kv % C::BK == 0 &&
+             (d.window <= 0 || (d.window % C::BQ == 0 && d.window >= 2 * C::BK));
+  if (!p.banded) return p;
+  p.own = C::BK / C::BQ;
+  p.wt = d.window > 0 ? int(std::min<int64_t>(d.window / C::BQ, INT32_MAX)) : INT32_MAX;
+  p.launches = (d.window > 0 && d.window < d.len_q) ? 3 : 2;
+  return p;
+}
+
 template <int D>
 dfa_status launch_dkdv(const dfa_attn_desc& d, BwdArgs a, hipStream_t s) {
   using C = DkvCfg<D, kDkvNW>;
   const int64_t nkb = cdiv(d.len_kv, C::BK);
+  const DkvPlan<D> p = dkdv_plan<D>(d);
   // Row split into the caller's workspace (sized by bwd_workspace_bytes and
   // checked before this call).
-  a.rsplit = dkdv_row_split<D>(d);
+  a.rsplit = p.rsplit;
   a.ws = a.rsplit > 1 ? static_cast<float*>(d.workspace) : nullptr;
   dim3 grid(unsigned(nkb) * unsigned(d.heads_kv), unsigned(d.batch), unsigned(a.rsplit));
   auto go = [&](auto kern, const BwdArgs& args) {
@@ -400,31 +434,19 @@ dfa_status launch_dkdv(const dfa_attn_desc& d, BwdArgs a, hipStream_t s) {
   if (pair_is_full(d, C::BK) && d.len_q % C::BQ == 0)
     return rsplit_reduce<D>(d, a, s, go(dkdv_bf16_kernel<D, kDkvNW, true, true>, a));
   const bool tm = d.window <= 0;
-  // A diagonal pair (query and key chunk the same tokens) of whole key
-  // blocks runs as row bands: each key block's first BK/BQ row tiles (its
-  // own rows, where the causal edge crosses it) and, with a window, the
-  // tiles from W rows past its first key on (where the window edge crosses
-  // it) in the masked kernel; the rows in between, which see every key of
-  // the block, in the mask-free one.  The bands add into dk, dv one after
-  // the other, so the result stays deterministic.
-  const int own = C::BK / C::BQ;
-  const bool banded = a.rsplit == 1 && d.causal && d.q_start == d.kv_start &&
-                      d.len_q == d.len_kv && d.len_kv % C::BK == 0 &&
-                      (d.window <= 0 || (d.window % C::BQ == 0 && d.window >= 2 * C::BK));
-  if (banded) {
-    const int wt = d.window > 0 ? int(std::min<int64_t>(d.window / C::BQ, INT32_MAX)) : INT32_MAX;
+  if (p.banded) {
     BwdArgs band = a;
     band.band_lo = 0;
-    band.band_hi = own;
+    band.band_hi = p.own;
     dfa_status st = tm ? go(dkdv_bf16_kernel<D, kDkvNW, false, true>, band)
                        : go(dkdv_bf16_kernel<D, kDkvNW, false, false>, band);
     if (st != DFA_OK) return st;
-    band.band_lo = own;
-    band.band_hi = wt;
+    band.band_lo = p.own;
+    band.band_hi = p.wt;
     st = tm ? go(dkdv_bf16_kernel<D, kDkvNW, true, true>, band)
             : go(dkdv_bf16_kernel<D, kDkvNW, true, false>, band);
-    if (st != DFA_OK || d.window <= 0 || d.window >= d.len_q) return st;
-    band.band_lo = wt;
+    if (st != DFA_OK || p.launches == 2) return st;
+    band.band_lo = p.wt;
     band.band_hi = INT32_MAX;
     return go(dkdv_bf16_kernel<D, kDkvNW, false, false>, band);
   }
@@ -450,6 +472,12 @@ dfa_status rsplit_reduce(const dfa_attn_desc& d, const BwdArgs& a, hipStream_t s
 dfa_status launch_dkdv_bf16(const dfa_attn_desc& d, const BwdArgs& a, hipStream_t s) {
   if (d.head_dim == 128) return launch_dkdv<128>(d, a, s);
   return launch_dkdv<64>(d, a, s);
+}
+
+int dkdv_launches(const dfa_attn_desc& d) {
+  if (d.batch == 0 || d.len_q == 0 || d.len_kv == 0) return 0;
+  if (d.dtype != DFA_BF16) return 1;
+  return d.head_dim == 128 ? dkdv_plan<128>(d).launches : dkdv_plan<64>(d).launches;
 }
 
 int64_t dkdv_split_bytes_per_slice(const dfa_attn_desc& d) {

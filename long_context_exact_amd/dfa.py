@@ -32,7 +32,7 @@ EXPORTED = (
     "dfa_attn_fwd_partial", "dfa_lse_merge", "dfa_attn_bwd", "dfa_attn_workspace_size",
     "dfa_chunk_transfer", "dfa_attn_fwd_partial_noalloc",
     "dfa_last_error", "dfa_version", "dfa_test_tile_shape", "dfa_test_fwd_tile_visits",
-    "dfa_test_bwd_part",
+    "dfa_test_bwd_part", "dfa_test_bwd_launches",
 )
 
 
@@ -95,6 +95,7 @@ def lib() -> ctypes.CDLL:
         L.dfa_test_fwd_tile_visits.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P]
         L.dfa_test_bwd_part.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, P, P, I32,
                                         P]
+        L.dfa_test_bwd_launches.argtypes = [ctypes.POINTER(AttnDesc), I32, ctypes.POINTER(I32)]
         L.dfa_attn_workspace_size.argtypes = [ctypes.POINTER(AttnDesc), I32, ctypes.POINTER(I64)]
         L.dfa_chunk_transfer.argtypes = [P, P, I64, P]
         L.dfa_attn_fwd_partial_noalloc.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P]
@@ -102,7 +103,7 @@ def lib() -> ctypes.CDLL:
                      "dfa_attn_fwd_partial", "dfa_lse_merge", "dfa_attn_workspace_size",
                      "dfa_chunk_transfer", "dfa_attn_fwd_partial_noalloc",
                      "dfa_attn_bwd", "dfa_test_tile_shape", "dfa_test_fwd_tile_visits",
-                     "dfa_test_bwd_part"):
+                     "dfa_test_bwd_part", "dfa_test_bwd_launches"):
             getattr(L, name).restype = I32
         L.dfa_last_error.argtypes = []
         L.dfa_last_error.restype = ctypes.c_char_p
@@ -326,6 +327,13 @@ def dfa_test_fwd_tile_visits(desc: AttnDesc, q, k, v, o_part, lse, visits, strea
             _ptr(visits, "visits", vshape, torch.uint8))
     d, _keep = _with_workspace(desc, DFA_OP_FWD, workspace, stream)
     _check(lib().dfa_test_fwd_tile_visits(ctypes.byref(d), *args, _stream(stream)))
+
+
+def dfa_test_bwd_launches(desc: AttnDesc, part: int) -> int:
+    """Kernel launches dfa_test_bwd_part makes for `part` (host only)."""
+    n = ctypes.c_int32(-1)
+    _check(lib().dfa_test_bwd_launches(ctypes.byref(desc), int(part), ctypes.byref(n)))
+    return n.value
 
 
 def dfa_test_bwd_part(desc: AttnDesc, q, k, v, lse, d_o, delta, dq, dk, dv, part: int,

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(dfa_lib):
 
 
 def test_version(dfa_lib):
-    assert dfa_lib.dfa_version() == 10000
+    assert dfa_lib.dfa_version() == 10100
 
 
 @pytest.mark.parametrize("p", list(range(1, 65)) + [127, 128, 1000])
@@ -277,6 +277,38 @@ def test_workspace_size_backward():
     assert n > 0 and n % (2 * 32768 * 8 * 128 * 4) == 0 and n <= 4 << 30
     assert D.dfa_attn_workspace_size(D.make_desc(1, 2, 2, 64, 4096, 64, dtype="f32"),
                                      D.DFA_OP_BWD) == 0
+
+
+def test_bwd_launch_counts(dfa_lib):
+    """dK/dV runs a diagonal pair of whole 256-key blocks as row bands (two
+    launches, three with a window of >= 512 rows, a multiple of 32, shorter
+    than the chunk) and everything else as one launch; dQ is always one
+    launch; a pair without rows or keys launches nothing."""
+    C = 32768
+    n = D.dfa_test_bwd_launches
+    full = D.make_desc(1, 64, 8, 128, C, C, 15 * C, 14 * C)
+    diag = D.make_desc(1, 64, 8, 128, C, C, 15 * C, 15 * C)
+    assert (n(full, 1), n(full, 2), n(diag, 1), n(diag, 2)) == (1, 1, 2, 1)
+    for win, want in ((4096, 3), (512, 3), (C, 2), (1 << 40, 2), (500, 1), (256, 1), (480, 1)):
+        d = D.make_desc(1, 64, 8, 128, C, C, 15 * C, 15 * C, window=win)
+        assert n(d, 1) == want, win
+    # a band pair of a window (not diagonal), a ragged diagonal, head_dim 64
+    assert n(D.make_desc(1, 64, 8, 128, C, C, 15 * C, 14 * C, window=4096), 1) == 1
+    assert n(D.make_desc(1, 8, 2, 128, 1000, 1000), 1) == 1
+    d64 = D.make_desc(1, 32, 8, 64, 16384, 16384)
+    assert D.dfa_attn_workspace_size(d64, D.DFA_OP_BWD) == 0 and n(d64, 1) == 2
+    # a diagonal whose rows the dK/dV kernel splits over workgroups does not band
+    split = D.make_desc(1, 8, 1, 128, 512, 512)
+    assert D.dfa_attn_workspace_size(split, D.DFA_OP_BWD) > 0 and n(split, 1) == 1
+    assert n(D.make_desc(1, 8, 2, 64, 1024, 1024, dtype="f32"), 1) == 1
+    for lq, lk in ((0, 256), (256, 0)):
+        e = D.make_desc(1, 4, 2, 128, lq, lk)
+        assert (n(e, 1), n(e, 2)) == (0, 0)
+    L = dfa_lib.lib()
+    c = ctypes.c_int32(0)
+    assert L.dfa_test_bwd_launches(ctypes.byref(diag), 3, ctypes.byref(c)) == D.DFA_ERR_INVALID
+    assert L.dfa_test_bwd_launches(ctypes.byref(diag), 1, None) == D.DFA_ERR_INVALID
+    assert L.dfa_test_bwd_launches(None, 1, ctypes.byref(c)) == D.DFA_ERR_INVALID
 
 
 def test_workspace_size_errors(dfa_lib):

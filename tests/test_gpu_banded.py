@@ -1,10 +1,11 @@
 """GPU parity of the backward of diagonal chunk pairs run as row bands.
 
 A diagonal pair (query and key chunk the same tokens) of whole 256-key
-blocks has its dK/dV computed in two launches, or three with a window that
-is a multiple of 32 rows and at least 512: each key block's own rows and,
-with a window, the rows past the window's reach in the masked kernel, the
-rows in between (which see every key of the block) in the mask-free one.
+blocks whose rows the kernel does not split has its dK/dV computed in two
+launches, or three with a window that is a multiple of 32 rows and at least
+512: each key block's own rows and, with a window, the rows past the
+window's reach in the masked kernel, the rows in between (which see every
+key of the block) in the mask-free one.
 Every gradient is compared element by element with the float64 oracle, on
 shapes that take the banded path and on one that just misses it (a window
 that is not a multiple of 32 rows), and repeated runs must agree bit for
@@ -28,23 +29,24 @@ def _need_gpu(dfa_lib):
         pytest.skip("no GPU")
 
 
-@pytest.mark.parametrize("l,start,hq,hkv,dh,win", [
-    (1024, 0, 8, 2, 128, 0),        # two bands: own rows masked, the rest mask-free
-    (1024, 0, 8, 2, 128, 512),      # three bands, the smallest window that bands
-    (1536, 3072, 4, 4, 64, 800),    # head_dim 64, non-zero chunk start, window of 25 tiles
-    (768, 0, 8, 1, 64, 0),          # one key/value head for eight query heads
-    (1280, 0, 4, 2, 128, 1024),     # window band reaching the chunk's end for late blocks
-    (1024, 0, 4, 2, 128, 500),      # not a multiple of 32 rows: one masked launch instead
+@pytest.mark.parametrize("b,l,start,hq,hkv,dh,win,launches", [
+    (2, 2048, 0, 16, 16, 128, 0, 2),       # own rows masked, the rest mask-free
+    (2, 2048, 0, 16, 16, 128, 512, 3),     # three bands, the smallest window that bands
+    (2, 2048, 4096, 16, 16, 64, 800, 3),   # head_dim 64, non-zero chunk start, 25-tile window
+    (16, 2048, 0, 8, 2, 64, 0, 2),         # four query heads per key/value head
+    (2, 2560, 0, 16, 16, 128, 1024, 3),    # late blocks' window band cut by the chunk's end
+    (2, 2048, 0, 16, 16, 128, 500, 1),     # not a multiple of 32 rows: one masked launch
 ])
-def test_banded_diagonal_pair_backward(l, start, hq, hkv, dh, win):
-    print(f"case banded {l} {start} {hq} {hkv} {dh} {win}", flush=True)
-    rng = np.random.default_rng(l * 131 + hq * 17 + dh + win)
+def test_banded_diagonal_pair_backward(b, l, start, hq, hkv, dh, win, launches):
+    print(f"case banded {b} {l} {start} {hq} {hkv} {dh} {win}", flush=True)
+    rng = np.random.default_rng(b * 7 + l * 131 + hq * 17 + dh + win)
     scale = dh ** -0.5
-    q = rand(rng, (1, l, hq, dh), "bf16")
-    k = rand(rng, (1, l, hkv, dh), "bf16")
-    v = rand(rng, (1, l, hkv, dh), "bf16")
-    d_o = rand(rng, (1, l, hq, dh), "bf16")
-    desc = D.make_desc(1, hq, hkv, dh, l, l, start, start, True, scale, "bf16", window=win)
+    q = rand(rng, (b, l, hq, dh), "bf16")
+    k = rand(rng, (b, l, hkv, dh), "bf16")
+    v = rand(rng, (b, l, hkv, dh), "bf16")
+    d_o = rand(rng, (b, l, hq, dh), "bf16")
+    desc = D.make_desc(b, hq, hkv, dh, l, l, start, start, True, scale, "bf16", window=win)
+    assert D.dfa_test_bwd_launches(desc, 1) == launches  # the path this case is for
     ro, rl = oracle.attention_fwd(q, k, v, scale, True, start, start, window=win)
     o_in = to_dev(ro.astype(np.float32), "bf16")
     lse_in = torch.from_numpy(rl.astype(np.float32)).to(DEV)
@@ -54,13 +56,13 @@ def test_banded_diagonal_pair_backward(l, start, hq, hkv, dh, win):
     runs = []
     for _ in range(2):
         delta = torch.empty_like(lse_in)
-        dq = torch.zeros(1, l, hq, dh, device=DEV)
-        dk = torch.zeros(1, l, hkv, dh, device=DEV)
-        dv = torch.zeros(1, l, hkv, dh, device=DEV)
+        dq = torch.zeros(b, l, hq, dh, device=DEV)
+        dk = torch.zeros(b, l, hkv, dh, device=DEV)
+        dv = torch.zeros(b, l, hkv, dh, device=DEV)
         D.dfa_attn_bwd(desc, qd, kd, vd, o_in, lse_in, dod, delta, True, dq, dk, dv)
         torch.cuda.synchronize()
         runs.append([to_np(x) for x in (dq, dk, dv)])
     for g, r, n in zip(runs[0], (rq, rk, rv), ("dQ", "dK", "dV")):
         check_grad(g, r, "bf16", n)
-    for a, b in zip(runs[0], runs[1]):
-        assert np.array_equal(a, b)
+    for x, y in zip(runs[0], runs[1]):
+        assert np.array_equal(x, y)
