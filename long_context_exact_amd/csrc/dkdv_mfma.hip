@@ -391,7 +391,6 @@ dfa_status rsplit_reduce(const dfa_attn_desc& d, const BwdArgs& a, hipStream_t s
 // in the masked kernel again.  The masked kernel's mask branch splits every
 // step's code, so it is kept to the steps that need it; the bands add into
 // dk, dv one after the other, so the result stays deterministic.
-template <int D>
 struct DkvPlan {
   int rsplit;    // row slices per key block (1: none)
   bool banded;
@@ -400,9 +399,9 @@ struct DkvPlan {
 };
 
 template <int D>
-DkvPlan<D> dkdv_plan(const dfa_attn_desc& d) {
+DkvPlan dkdv_plan(const dfa_attn_desc& d) {
   using C = DkvCfg<D, kDkvNW>;
-  DkvPlan<D> p{dkdv_row_split<D>(d), false, 0, INT32_MAX, 1};
+  DkvPlan p{dkdv_row_split<D>(d), false, 0, INT32_MAX, 1};
   if (pair_is_full(d, C::BK) && d.len_q % C::BQ == 0) return p;
   p.banded = p.rsplit == 1 && d.causal && d.q_start == d.kv_start && d.len_q == d.len_kv &&
              d.len_kv % C::BK == 0 &&
@@ -418,7 +417,7 @@ template <int D>
 dfa_status launch_dkdv(const dfa_attn_desc& d, BwdArgs a, hipStream_t s) {
   using C = DkvCfg<D, kDkvNW>;
   const int64_t nkb = cdiv(d.len_kv, C::BK);
-  const DkvPlan<D> p = dkdv_plan<D>(d);
+  const DkvPlan p = dkdv_plan<D>(d);
   // Row split into the caller's workspace (sized by bwd_workspace_bytes and
   // checked before this call).
   a.rsplit = p.rsplit;
