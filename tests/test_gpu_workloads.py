@@ -8,10 +8,12 @@ any size instead:
   sum_j dK_j = 0 (each row's dS sums to zero),
 plus exact dK/dV rows for sampled keys where the rows that see them fit.
 
-For the worker shares, dK and dV of every key are also compared element
-by element: a second backward with dO zero outside 64 sampled rows makes
-every key's gradient exactly those rows' contribution, which the oracle
-computes from them alone.
+For the 65536-token sequence and the worker shares, dK and dV of every key
+are also compared element by element: a second backward with dO zero
+outside 64 sampled rows makes every key's gradient exactly those rows'
+contribution, which the oracle computes from them alone.  For the
+forward-only sequence, the last chunk's merged O and LSE are compared whole
+in two heads.
 
 Sizes: 32768-token sequence (8 x 4096, forward only), 65536 (8 x 8192,
 forward + backward), and worker 15's query chunk at 16 x 16384 (32 heads)
@@ -127,6 +129,14 @@ def test_llama7b_32k_forward():
     c = w.chunk
     for a in (0, 3, 7):
         _check_rows(w, host, res, a, [0, 1, c // 2 + 5, c - 1], [0, w.heads_q - 1], False)
+    # the last chunk's merged O and LSE whole (every row) in two heads
+    for h in (0, w.heads_q - 1):
+        kp, vp = _prefix(host, 1, 7, h), _prefix(host, 2, 7, h)
+        qa = host[0][7][:, :, h:h + 1].astype(np.float64)
+        ro, rl = oracle.attention_fwd(qa, kp, vp, w.scale, True, 7 * c, 0)
+        got = to_np(res["o"][7][:, :, h:h + 1])
+        assert np.max(np.abs(got - ro)) <= 1e-2 and rel_fro(got, ro) <= 2e-2, h
+        check_lse(to_np(res["lse"][7][:, h:h + 1, :]), rl, "bf16", f"LSE chunk 7 head {h}")
     # one full and one diagonal partial, sampled rows against that pair alone
     for a, cc in ((7, 0), (7, 7)):
         op, lp = res["partials"][(a, cc)]
@@ -168,6 +178,10 @@ def test_llama7b_64k_forward_backward():
         want_v.append(rv.ravel())
     assert rel_fro(np.concatenate(got_k), np.concatenate(want_k)) <= 2e-2
     assert rel_fro(np.concatenate(got_v), np.concatenate(want_v)) <= 2e-2
+    # every key of every chunk, element by element: the backward of the last
+    # chunk's 8 pairs (its diagonal pair in row bands) from 64 sampled rows
+    runs = [(0, 16), (c // 3 + 5, 16), (2 * c // 3 + 11, 16), (c - 16, 16)]
+    _check_dkdv_sparse_do(w, att, host, res, 7, att.items_of_owner(7), [0, w.heads_q - 1], runs)
 
 
 def _check_dkdv_sparse_do(w, att, host, res, a, items, heads, runs):
