@@ -185,7 +185,8 @@ def test_llama7b_64k_forward_backward():
 
 
 def _check_dkdv_sparse_do(w, att, host, res, a, items, heads, runs):
-    """dK / dV of every key of every key/value chunk, element by element.
+    """dK / dV of every key of every key/value chunk, element by element, and
+    O and dQ of the sampled rows.
 
     The backward is run again with dO zero except on the sampled query rows
     (`runs`: (first row, count) of chunk a) of the sampled heads.  Every
@@ -207,6 +208,7 @@ def _check_dkdv_sparse_do(w, att, host, res, a, items, heads, runs):
     delta = {a: torch.empty(att.lse_shape(), device=DEV)}
     att.backward_items(items, dev[0], dev[1], dev[2], res["o"], res["lse"], d_o, delta, dq, dk, dv)
     torch.cuda.synchronize()
+    got_o, want_o, got_q, want_q = [], [], [], []
     for g in sorted({h // grp for h in heads}):
         kp, vp = _prefix(host, 1, a, g), _prefix(host, 2, a, g)
         want_k, want_v = np.zeros_like(kp), np.zeros_like(vp)
@@ -215,10 +217,15 @@ def _check_dkdv_sparse_do(w, att, host, res, a, items, heads, runs):
                 qr = host[0][a][:, r0:r0 + n, h:h + 1].astype(np.float64)
                 dor = host[3][a][:, r0:r0 + n, h:h + 1].astype(np.float64)
                 ro, rl = oracle.attention_fwd(qr, kp, vp, w.scale, True, a * c + r0, 0)
-                _, rk, rv = oracle.attention_bwd(qr, kp, vp, ro, rl, dor, w.scale, True,
-                                                 a * c + r0, 0)
+                rq, rk, rv = oracle.attention_bwd(qr, kp, vp, ro, rl, dor, w.scale, True,
+                                                  a * c + r0, 0)
                 want_k += rk
                 want_v += rv
+                # the sampled rows' O, and their dQ (a row's dQ depends on its own dO only)
+                got_o.append(to_np(res["o"][a][:, r0:r0 + n, h:h + 1]))
+                want_o.append(ro)
+                got_q.append(to_np(dq[a][:, r0:r0 + n, h:h + 1]))
+                want_q.append(rq)
         for j in kvs:
             for name, got_t, want in (("dK", dk, want_k), ("dV", dv, want_v)):
                 got = to_np(got_t[j][:, :, g])
@@ -228,6 +235,12 @@ def _check_dkdv_sparse_do(w, att, host, res, a, items, heads, runs):
                 print(f"  {name} chunk {j} kv head {g}: rel fro {r:.2e}, max err / max {m:.2e}",
                       flush=True)
                 assert r <= 2e-2 and m <= 2e-2, (name, j, g, r, m)
+    go, wo = np.concatenate(got_o, 1), np.concatenate(want_o, 1)
+    gq, wq = np.concatenate(got_q, 1), np.concatenate(want_q, 1)
+    print(f"  O of the sampled rows: max abs {np.max(np.abs(go - wo)):.2e}; dQ rel fro "
+          f"{rel_fro(gq, wq):.2e}", flush=True)
+    assert np.max(np.abs(go - wo)) <= 1e-2 and rel_fro(go, wo) <= 2e-2
+    assert rel_fro(gq, wq) <= 2e-2
     # the other kv heads saw no sampled row: exactly zero
     for j in kvs:
         for g in set(range(w.heads_kv)) - {h // grp for h in heads}:
