@@ -8,8 +8,9 @@ any size instead:
   sum_j dK_j = 0 (each row's dS sums to zero),
 plus exact dK/dV rows for sampled keys where the rows that see them fit.
 
-For the 65536-token sequence and the worker shares, dK and dV of every key
-are also compared element by element: a second backward with dO zero
+For the 65536-token sequence and the worker shares (also under a window
+and with global tokens), dK and dV of every key are also compared element
+by element: a second backward with dO zero
 outside 64 sampled rows makes every key's gradient exactly those rows'
 contribution, which the oracle computes from them alone.  For the
 forward-only sequence, the last chunk's merged O and LSE are compared whole
@@ -184,7 +185,8 @@ def test_llama7b_64k_forward_backward():
     _check_dkdv_sparse_do(w, att, host, res, 7, att.items_of_owner(7), [0, w.heads_q - 1], runs)
 
 
-def _check_dkdv_sparse_do(w, att, host, res, a, items, heads, runs):
+def _check_dkdv_sparse_do(w, att, host, res, a, items, heads, runs, keys=None, kv_bufs=None,
+                          **okw):
     """dK / dV of every key of every key/value chunk, element by element, and
     O and dQ of the sampled rows.
 
@@ -194,14 +196,22 @@ def _check_dkdv_sparse_do(w, att, host, res, a, items, heads, runs):
     dS = P (dP - delta) = 0, so it adds nothing: each key's dK and dV are
     exactly the sampled rows' contributions, which the oracle computes from
     those rows alone (their own full-prefix O and LSE).  The launch
-    configuration is the one the bench times (same pairs, same kernels)."""
+    configuration is the one the bench times (same pairs, same kernels).
+    keys(g) -> (K, V, first key position, {chunk: columns}) gives the oracle
+    its keys (default: the whole prefix of chunk a); kv_bufs the chunks
+    whose dK / dV buffers the pairs add into (default: the pairs' chunks);
+    okw the oracle's window / global-token arguments."""
     c, grp, dev = w.chunk, w.heads_q // w.heads_kv, res["dev"]
     sparse = np.zeros((w.batch, c, w.heads_q, w.head_dim), dtype=np.float32)
     for h in heads:
         for r0, n in runs:
             sparse[:, r0:r0 + n, h] = host[3][a][:, r0:r0 + n, h]
     d_o = {a: torch.from_numpy(sparse).to(DEV).to(TD[w.dtype])}
-    kvs = sorted({it[3] for it in items})
+    kvs = kv_bufs if kv_bufs is not None else sorted({it[3] for it in items})
+    if keys is None:
+        def keys(g):
+            return (_prefix(host, 1, a, g), _prefix(host, 2, a, g), 0,
+                    {j: slice(j * c, (j + 1) * c) for j in kvs})
     dq = {a: torch.zeros(att.q_shape(), device=DEV)}
     dk = {j: torch.zeros(att.kv_shape(), device=DEV) for j in kvs}
     dv = {j: torch.zeros(att.kv_shape(), device=DEV) for j in kvs}
@@ -210,15 +220,15 @@ def _check_dkdv_sparse_do(w, att, host, res, a, items, heads, runs):
     torch.cuda.synchronize()
     got_o, want_o, got_q, want_q = [], [], [], []
     for g in sorted({h // grp for h in heads}):
-        kp, vp = _prefix(host, 1, a, g), _prefix(host, 2, a, g)
+        kp, vp, k0, cols = keys(g)
         want_k, want_v = np.zeros_like(kp), np.zeros_like(vp)
         for h in (x for x in heads if x // grp == g):
             for r0, n in runs:
                 qr = host[0][a][:, r0:r0 + n, h:h + 1].astype(np.float64)
                 dor = host[3][a][:, r0:r0 + n, h:h + 1].astype(np.float64)
-                ro, rl = oracle.attention_fwd(qr, kp, vp, w.scale, True, a * c + r0, 0)
+                ro, rl = oracle.attention_fwd(qr, kp, vp, w.scale, True, a * c + r0, k0, **okw)
                 rq, rk, rv = oracle.attention_bwd(qr, kp, vp, ro, rl, dor, w.scale, True,
-                                                  a * c + r0, 0)
+                                                  a * c + r0, k0, **okw)
                 want_k += rk
                 want_v += rv
                 # the sampled rows' O, and their dQ (a row's dQ depends on its own dO only)
@@ -229,7 +239,7 @@ def _check_dkdv_sparse_do(w, att, host, res, a, items, heads, runs):
         for j in kvs:
             for name, got_t, want in (("dK", dk, want_k), ("dV", dv, want_v)):
                 got = to_np(got_t[j][:, :, g])
-                ref = want[:, j * c:(j + 1) * c, 0]
+                ref = want[:, cols[j], 0]
                 r = rel_fro(got, ref)
                 m = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
                 print(f"  {name} chunk {j} kv head {g}: rel fro {r:.2e}, max err / max {m:.2e}",
@@ -277,8 +287,8 @@ def test_worker_share_forward_backward(name):
 def test_windowed_worker_share_forward_backward():
     """Worker 15's share under a 4096-token sliding window (App. F): the
     window schedule gives it (15, 15) and (15, 14) only; sampled rows of the
-    merged O / LSE and of dQ against the oracle over each row's window, and
-    the dK / dV identities over the two key chunks."""
+    merged O / LSE and of dQ against the oracle over each row's window, the
+    dK / dV identities over the two key chunks, and every key's dK / dV."""
     w = WORKLOADS["gqa64x8_512k_win4k_w15"]
     print(f"case {w.name}", flush=True)
     att = ChunkedCausalAttention(w.workers, w.chunk, w.batch, w.heads_q, w.heads_kv, w.head_dim,
@@ -314,14 +324,26 @@ def test_windowed_worker_share_forward_backward():
     assert rel_fro(np.concatenate(got_dq), np.concatenate(want_dq)) <= 2e-2
     _check_grad_identities(w, host, res, [a], kvs)
 
+    # every key's dK / dV of the two window chunks (the diagonal pair's dK/dV
+    # in three row bands), from 64 sampled rows on both sides of the window's
+    # reach
+    def keys(g):
+        kp = np.concatenate([host[1][j][:, :, g:g + 1] for j in kvs], 1).astype(np.float64)
+        vp = np.concatenate([host[2][j][:, :, g:g + 1] for j in kvs], 1).astype(np.float64)
+        return kp, vp, (a - 1) * c, {a - 1: slice(0, c), a: slice(c, 2 * c)}
+
+    heads = [0, 1, grp + 1, w.heads_q - 1]
+    runs = [(0, 16), (win - 8, 16), (c // 2 + 3, 16), (c - 16, 16)]
+    _check_dkdv_sparse_do(w, att, host, res, a, items, heads, runs, keys=keys, window=win)
+
 
 def test_global_window_worker_share_forward_backward():
     """Worker 15's share with a 4096-token window and the first 1024 tokens
     global (App. F, replicated): its global item (the 1024 global keys, read
     from chunk 0) and its window pairs (15, 14), (15, 15); sampled rows of the
     merged O / LSE and of dQ against the oracle's plain definition over the
-    whole prefix, and the dK / dV identities over chunk 0 and the two window
-    chunks.  Chunks 1..13 hold neither global tokens nor keys inside these
+    whole prefix, the dK / dV identities over chunk 0 and the two window
+    chunks, and every key's dK / dV.  Chunks 1..13 hold neither global tokens nor keys inside these
     rows' windows: they enter the oracle as zeros, which its mask drops."""
     w = WORKLOADS["gqa64x8_512k_win4k_g1k_w15"]
     print(f"case {w.name}", flush=True)
@@ -362,3 +384,16 @@ def test_global_window_worker_share_forward_backward():
     _check_grad_identities(w, host, res, [a], kvs)
     # keys of chunk 0 past the global prefix are seen by no row of this share
     assert torch.all(res["dv"][0][:, g:] == 0) and torch.all(res["dk"][0][:, g:] == 0)
+
+    # every key's dK / dV of the global prefix and the two window chunks
+    def keys(hk):
+        kp = np.concatenate([host[1][j][:, :, hk:hk + 1].astype(np.float64) if j in kvs
+                             else zeros for j in range(a + 1)], 1)
+        vp = np.concatenate([host[2][j][:, :, hk:hk + 1].astype(np.float64) if j in kvs
+                             else zeros for j in range(a + 1)], 1)
+        return kp, vp, 0, {j: slice(j * c, (j + 1) * c) for j in kvs}
+
+    heads = [0, 1, grp + 1, w.heads_q - 1]
+    runs = [(0, 16), (win - 8, 16), (c // 2 + 3, 16), (c - 16, 16)]
+    _check_dkdv_sparse_do(w, att, host, res, a, items, heads, runs, keys=keys, kv_bufs=kvs,
+                          window=win, n_global=g)
