@@ -232,7 +232,9 @@ def test_forward_and_backward_are_deterministic_and_remat_free():
             assert np.array_equal(r1[key][a], r2[key][a]), key
 
 
-@pytest.mark.parametrize("n,out", [(1, "f32"), (3, "bf16"), (16, "f32"), (16, "bf16"), (64, "f32")])
+# n below, at, and past multiples of the merge's eight partials per load group
+@pytest.mark.parametrize("n,out", [(1, "f32"), (3, "bf16"), (8, "f32"), (9, "bf16"), (16, "f32"),
+                                   (16, "bf16"), (17, "f32"), (64, "f32")])
 def test_merge_parity(n, out):
     rng = np.random.default_rng(n)
     b, lq, h, dh = 2, 77, 3, 128
