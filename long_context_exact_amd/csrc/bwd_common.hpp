@@ -34,6 +34,10 @@ struct BwdArgs {
   // first visible row), only tiles [band_lo, band_hi) run in this launch, so
   // that one pair can run as bands of different kernels (0, INT32_MAX: all).
   int32_t band_lo, band_hi;
+  // Paired launch of a windowed diagonal pair's two masked bands: the
+  // window-edge rows start pair_wt row tiles past each key block's first row
+  // (0 for every other launch).
+  int32_t pair_wt;
 };
 
 // The query-row steps of the dK/dV workgroup owning keys [k_lo, k_lo + bk):

@@ -53,6 +53,7 @@ BwdArgs bwd_args_of(const dfa_attn_desc& d) {
   a.ws = nullptr;
   a.band_lo = 0;  // and may run a pair as row bands
   a.band_hi = INT32_MAX;
+  a.pair_wt = 0;
   return a;
 }
 

@@ -27,16 +27,28 @@ struct DkvCfg {
   static constexpr int STATS = 2 * BQ;           // -log2 LSE and delta of a step's rows (floats)
   static constexpr int STAGE = 2 * Q_TILE + 2 * STATS;  // Q + dO + row statistics (16-bit units)
   static constexpr int LDS_BYTES = (KV_TILE + 2 * STAGE) * 2;
+  // Paired row bands (see the kernel): two tiles' Q, dO and statistics per stage.
+  static constexpr int LDS_BYTES_PAIR = (KV_TILE + 4 * STAGE) * 2;
+  static constexpr int NPAIR = BK / BQ + 1;  // steps per head of a paired launch
   static_assert(KV_SEGS % NW == 0, "key tile segments must divide over the waves");
   static_assert((2 * Q_SEGS) % NW == 0, "Q and dO segments divide over the waves");
-  static_assert(LDS_BYTES <= 160 * 1024, "fits gfx950 LDS");
+  static_assert(LDS_BYTES <= 160 * 1024 && LDS_BYTES_PAIR <= 160 * 1024, "fits gfx950 LDS");
 };
 
 // TM: tile-major step order (see tile_of below), for pairs without a window.
-template <int D, int NW, bool FULL, bool TM>
+// PAIR: the two masked row bands of a windowed diagonal pair in one launch.
+// Of a key block's own row tiles (0 .. BK/BQ - 1 from its first row, where
+// the causal edge crosses it) wave w sees only tiles t >= w, and of the
+// tiles at the window's edge (a.pair_wt + t) only t <= w.  Step p of a head
+// stages own tile p - 1 and edge tile p together, and each wave takes the
+// one of the two it sees (own if p - 1 >= w, else edge): BK/BQ + 1 steps per
+// head in which every wave works, against 2 * BK/BQ steps run as two bands
+// in which half the waves idle on average.
+template <int D, int NW, bool FULL, bool TM, bool PAIR = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DFA_BWD_OCC, DFA_BWD_OCC)))
 void dkdv_bf16_kernel(BwdArgs a) {
   using C = DkvCfg<D, NW>;
+  static_assert(!PAIR || (!FULL && !TM), "paired bands run the masked, head-major kernel");
   extern __shared__ __align__(16) uint16_t smem_generic[];
   lds_u16* smem = lds_base(smem_generic);
   lds_u16* Vs = smem;
@@ -62,9 +74,10 @@ void dkdv_bf16_kernel(BwdArgs a) {
   // split the blockIdx.z-th slice of them (uniform over the workgroup).
   const DkvSpan sp = dkdv_span(a, k_lo, C::BK, C::BQ);
   const int qt0 = sp.qt0, nq = sp.nq;
-  const int per = int(cdiv(sp.steps, a.rsplit));
+  const int n_steps = PAIR ? (sp.steps > 0 ? C::NPAIR * a.group : 0) : sp.steps;
+  const int per = int(cdiv(n_steps, a.rsplit));
   const int it0 = int(blockIdx.z) * per;
-  const int it1 = min(sp.steps, it0 + per);
+  const int it1 = min(n_steps, it0 + per);
   if (it0 >= it1) return;  // the reduction skips slices without steps
   // Step it covers query tile tile_of(it) of head head_of(it).  Without a
   // window every key block's rows end at the chunk's end: tiles run from the
@@ -75,7 +88,18 @@ void dkdv_bf16_kernel(BwdArgs a) {
   // key block: heads outermost, tiles ascending, keeps neighbouring blocks a
   // few steps apart in the same head's rows instead.
   auto tile_of = [&](int it) { return TM ? qt0 + nq - 1 - it / a.group : qt0 + it % nq; };
-  auto head_of = [&](int it) { return g * a.group + (TM ? it % a.group : it / nq); };
+  auto head_of = [&](int it) {
+    return g * a.group + (TM ? it % a.group : it / (PAIR ? C::NPAIR : nq));
+  };
+  // PAIR: the own and the edge tile of step it (tile indices from the chunk's
+  // first row) and whether each holds rows of this key block's span.
+  auto pair_tiles = [&](int it, int& own_t, int& edge_t, bool& own_ok, bool& edge_ok) {
+    const int pp = it % C::NPAIR;
+    own_t = qt0 + pp - 1;
+    edge_t = qt0 + a.pair_wt + pp;
+    own_ok = pp >= 1 && pp - 1 < nq;
+    edge_ok = pp <= C::NPAIR - 2 && a.pair_wt + pp < nq;
+  };
 
   // K of this lane's key as the B operand of S (elements d = 16*st + 8*hi
   // + e), in VGPRs for the whole loop; V rows of the workgroup in LDS.
@@ -102,8 +126,41 @@ void dkdv_bf16_kernel(BwdArgs a) {
     dv_acc[db] = f32x16{};
   }
 
-  auto stage_ptr = [&](int stage) { return smem + C::KV_TILE + stage * C::STAGE; };
+  auto stage_ptr = [&](int stage) {
+    return smem + C::KV_TILE + stage * (PAIR ? 2 * C::STAGE : C::STAGE);
+  };
+  auto stage_q_pair = [&](int it, int stage) {
+    const int h = head_of(it);
+    int own_t, edge_t;
+    bool own_ok, edge_ok;
+    pair_tiles(it, own_t, edge_t, own_ok, edge_ok);
+    const uint16_t* qb = a.q + b * a.len_q * q_rs + int64_t(h) * D;
+    const uint16_t* db_ = a.d_o + b * a.len_q * q_rs + int64_t(h) * D;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    // 4 * Q_SEGS segments (own Q, own dO, edge Q, edge dO) spread over the
+    // waves; a tile without rows of the span is not staged (no wave reads it)
+#pragma unroll
+    for (int i = 0; i < 4 * C::Q_SEGS / NW; ++i) {
+      const int seg = wave + i * NW;
+      const int half = seg / (2 * C::Q_SEGS);
+      const int s2 = seg - half * 2 * C::Q_SEGS;
+      if (!(half == 0 ? own_ok : edge_ok)) continue;
+      const int64_t i0 = int64_t(half == 0 ? own_t : edge_t) * C::BQ;
+      const int last_row = int(min<int64_t>(a.len_q - 1 - i0, C::BQ - 1));
+      lds_u16* Qs = stage_ptr(stage) + half * C::STAGE;
+      if (s2 < C::Q_SEGS)
+        tile_dma_rows<D>(Qs, s2, ln, qb + i0 * q_rs, uint32_t(q_rs * 2), last_row);
+      else
+        tile_dma_rows<D>(Qs + C::Q_TILE, s2 - C::Q_SEGS, ln, db_ + i0 * q_rs, uint32_t(q_rs * 2),
+                         last_row);
+    }
+  };
   auto stage_q = [&](int it, int stage) {
+    if constexpr (PAIR) {
+      stage_q_pair(it, stage);
+      return;
+    }
     const int h = head_of(it);
     const int64_t i0 = int64_t(tile_of(it)) * C::BQ;
     const uint16_t* qb = a.q + b * a.len_q * q_rs + int64_t(h) * D;
@@ -139,6 +196,18 @@ void dkdv_bf16_kernel(BwdArgs a) {
   bool raw_ok = false;
   auto load_stats = [&](int it) {
     const int h = head_of(it);
+    if constexpr (PAIR) {  // lanes 0..31: the own tile's rows, 32..63: the edge tile's
+      int own_t, edge_t;
+      bool own_ok, edge_ok;
+      pair_tiles(it, own_t, edge_t, own_ok, edge_ok);
+      const bool edge = lane >= C::BQ;
+      const int64_t row = int64_t(edge ? edge_t : own_t) * C::BQ + (lane & (C::BQ - 1));
+      raw_ok = (edge ? edge_ok : own_ok) && row >= 0 && row < a.len_q;
+      const int64_t li = (b * a.hq + h) * a.len_q + min<int64_t>(max<int64_t>(row, 0), a.len_q - 1);
+      raw_l = a.lse[li];
+      raw_d = a.delta[li];
+      return;
+    }
     const int64_t row = int64_t(tile_of(it)) * C::BQ + lane;
     raw_ok = lane < C::BQ && (FULL || row < a.len_q);
     const int64_t li = (b * a.hq + h) * a.len_q + min<int64_t>(row, a.len_q - 1);
@@ -150,6 +219,14 @@ void dkdv_bf16_kernel(BwdArgs a) {
     // every row of a fully visible pair sees keys, so its LSE is finite
     const float nl = (FULL || x > -INFINITY) ? -x * kLog2e : -INFINITY;
     const float dl = raw_ok ? raw_d : 0.f;
+    if constexpr (PAIR) {
+      static_assert(2 * C::BQ == 64, "one lane per row of the two tiles");
+      lds_f32* st = reinterpret_cast<lds_f32*>(stage_ptr(stage) + (lane >= C::BQ ? C::STAGE : 0) +
+                                               2 * C::Q_TILE);
+      st[lane & (C::BQ - 1)] = nl;
+      st[C::BQ + (lane & (C::BQ - 1))] = dl;
+      return;
+    }
     lds_f32* st = reinterpret_cast<lds_f32*>(stage_ptr(stage) + 2 * C::Q_TILE);
     if (lane < C::BQ) {
       st[lane] = nl;
@@ -171,10 +248,21 @@ void dkdv_bf16_kernel(BwdArgs a) {
       if (wave == 0) load_stats(it + 1);
     }
     const lds_u16* Qs = stage_ptr(stage);
+    int64_t r0;  // first row of this step's tile (for this wave)
+    bool any = wave_active;
+    if constexpr (PAIR) {
+      int own_t, edge_t;
+      bool own_ok, edge_ok;
+      pair_tiles(it, own_t, edge_t, own_ok, edge_ok);
+      const bool own = it % C::NPAIR - 1 >= wave;  // this wave's keys are seen by the own tile
+      if (!own) Qs += C::STAGE;
+      r0 = int64_t(own ? own_t : edge_t) * C::BQ;
+      if (!(own ? own_ok : edge_ok)) any = false;
+    } else {
+      r0 = int64_t(tile_of(it)) * C::BQ;
+    }
     const lds_u16* dOs = Qs + C::Q_TILE;
     const lds_f32* stats = reinterpret_cast<const lds_f32*>(Qs + 2 * C::Q_TILE);
-    const int64_t r0 = int64_t(tile_of(it)) * C::BQ;  // first row of this step
-    bool any = wave_active;
     if constexpr (!FULL) {
       if (any && a.causal) any = a.q_start + min<int64_t>(r0 + C::BQ, a.len_q) - 1 >= a.kv_start + wk_lo;
       if (any) any = a.q_start + r0 - (a.kv_start + wk_hi - 1) < a.win;
@@ -387,13 +475,16 @@ dfa_status rsplit_reduce(const dfa_attn_desc& d, const BwdArgs& a, hipStream_t s
 // every key block: the block's own BK/BQ row tiles (where the causal edge
 // crosses it) in the masked kernel, the rows from there to W rows past its
 // first key (every one of which sees all its keys) in the mask-free kernel,
-// and, with a window, the rows from W on (where the window edge crosses it)
-// in the masked kernel again.  The masked kernel's mask branch splits every
-// step's code, so it is kept to the steps that need it; the bands add into
-// dk, dv one after the other, so the result stays deterministic.
+// and, with a window shorter than the chunk, the rows from W on (where the
+// window edge crosses it) in the masked kernel too, paired with the own
+// rows in one launch (see the kernel's PAIR mode).  The masked kernel's mask
+// branch splits every step's code, so it is kept to the steps that need it;
+// the bands add into dk, dv one after the other, so the result stays
+// deterministic.
 struct DkvPlan {
   int rsplit;    // row slices per key block (1: none)
   bool banded;
+  bool paired;   // the own and the window-edge rows in one paired launch
   int own, wt;   // band limits in row tiles: [0, own) masked, [own, wt) mask-free, [wt, ..) masked
   int launches;  // dK/dV kernel launches (the split reduction not counted)
 };
@@ -401,7 +492,7 @@ struct DkvPlan {
 template <int D>
 DkvPlan dkdv_plan(const dfa_attn_desc& d) {
   using C = DkvCfg<D, kDkvNW>;
-  DkvPlan p{dkdv_row_split<D>(d), false, 0, INT32_MAX, 1};
+  DkvPlan p{dkdv_row_split<D>(d), false, false, 0, INT32_MAX, 1};
   if (pair_is_full(d, C::BK) && d.len_q % C::BQ == 0) return p;
   p.banded = p.rsplit == 1 && d.causal && d.q_start == d.kv_start && d.len_q == d.len_kv &&
              d.len_kv % C::BK == 0 &&
@@ -409,7 +500,8 @@ DkvPlan dkdv_plan(const dfa_attn_desc& d) {
   if (!p.banded) return p;
   p.own = C::BK / C::BQ;
   p.wt = d.window > 0 ? int(std::min<int64_t>(d.window / C::BQ, INT32_MAX)) : INT32_MAX;
-  p.launches = (d.window > 0 && d.window < d.len_q) ? 3 : 2;
+  p.paired = d.window > 0 && d.window < d.len_q;
+  p.launches = 2;
   return p;
 }
 
@@ -423,10 +515,10 @@ dfa_status launch_dkdv(const dfa_attn_desc& d, BwdArgs a, hipStream_t s) {
   a.rsplit = p.rsplit;
   a.ws = a.rsplit > 1 ? static_cast<float*>(d.workspace) : nullptr;
   dim3 grid(unsigned(nkb) * unsigned(d.heads_kv), unsigned(d.batch), unsigned(a.rsplit));
-  auto go = [&](auto kern, const BwdArgs& args) {
-    const dfa_status st = allow_lds(kern, C::LDS_BYTES, "dkdv_bf16_kernel");
+  auto go = [&](auto kern, const BwdArgs& args, int lds_bytes = C::LDS_BYTES) {
+    const dfa_status st = allow_lds(kern, lds_bytes, "dkdv_bf16_kernel");
     if (st != DFA_OK) return st;
-    hipLaunchKernelGGL(kern, grid, dim3(C::NT), C::LDS_BYTES, s, args);
+    hipLaunchKernelGGL(kern, grid, dim3(C::NT), lds_bytes, s, args);
     return check_launch("dkdv_bf16_kernel");
   };
   // a fully visible pair's key blocks all run the same rows: tile-major order
@@ -435,19 +527,22 @@ dfa_status launch_dkdv(const dfa_attn_desc& d, BwdArgs a, hipStream_t s) {
   const bool tm = d.window <= 0;
   if (p.banded) {
     BwdArgs band = a;
-    band.band_lo = 0;
-    band.band_hi = p.own;
-    dfa_status st = tm ? go(dkdv_bf16_kernel<D, kDkvNW, false, true>, band)
-                       : go(dkdv_bf16_kernel<D, kDkvNW, false, false>, band);
+    dfa_status st;
+    if (p.paired) {  // own rows and window-edge rows, paired (whole span, masked)
+      band.pair_wt = p.wt;
+      st = go(dkdv_bf16_kernel<D, kDkvNW, false, false, true>, band, C::LDS_BYTES_PAIR);
+      band.pair_wt = 0;
+    } else {
+      band.band_lo = 0;
+      band.band_hi = p.own;
+      st = tm ? go(dkdv_bf16_kernel<D, kDkvNW, false, true>, band)
+              : go(dkdv_bf16_kernel<D, kDkvNW, false, false>, band);
+    }
     if (st != DFA_OK) return st;
     band.band_lo = p.own;
     band.band_hi = p.wt;
-    st = tm ? go(dkdv_bf16_kernel<D, kDkvNW, true, true>, band)
-            : go(dkdv_bf16_kernel<D, kDkvNW, true, false>, band);
-    if (st != DFA_OK || p.launches == 2) return st;
-    band.band_lo = p.wt;
-    band.band_hi = INT32_MAX;
-    return go(dkdv_bf16_kernel<D, kDkvNW, false, false>, band);
+    return tm ? go(dkdv_bf16_kernel<D, kDkvNW, true, true>, band)
+              : go(dkdv_bf16_kernel<D, kDkvNW, true, false>, band);
   }
   return rsplit_reduce<D>(d, a, s,
                           tm ? go(dkdv_bf16_kernel<D, kDkvNW, false, true>, a)

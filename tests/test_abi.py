@@ -280,16 +280,17 @@ def test_workspace_size_backward():
 
 
 def test_bwd_launch_counts(dfa_lib):
-    """dK/dV runs a diagonal pair of whole 256-key blocks as row bands (two
-    launches, three with a window of >= 512 rows, a multiple of 32, shorter
-    than the chunk) and everything else as one launch; dQ is always one
-    launch; a pair without rows or keys launches nothing."""
+    """dK/dV runs a diagonal pair of whole 256-key blocks as two row-band
+    launches (with a window of >= 512 rows, a multiple of 32, shorter than
+    the chunk, the first pairs each block's own rows with its window-edge
+    rows) and everything else as one launch; dQ is always one launch; a pair
+    without rows or keys launches nothing."""
     C = 32768
     n = D.dfa_test_bwd_launches
     full = D.make_desc(1, 64, 8, 128, C, C, 15 * C, 14 * C)
     diag = D.make_desc(1, 64, 8, 128, C, C, 15 * C, 15 * C)
     assert (n(full, 1), n(full, 2), n(diag, 1), n(diag, 2)) == (1, 1, 2, 1)
-    for win, want in ((4096, 3), (512, 3), (C, 2), (1 << 40, 2), (500, 1), (256, 1), (480, 1)):
+    for win, want in ((4096, 2), (512, 2), (C, 2), (1 << 40, 2), (500, 1), (256, 1), (480, 1)):
         d = D.make_desc(1, 64, 8, 128, C, C, 15 * C, 15 * C, window=win)
         assert n(d, 1) == want, win
     # a band pair of a window (not diagonal), a ragged diagonal, head_dim 64

@@ -2,10 +2,11 @@
 
 A diagonal pair (query and key chunk the same tokens) of whole 256-key
 blocks whose rows the kernel does not split has its dK/dV computed in two
-launches, or three with a window that is a multiple of 32 rows and at least
-512: each key block's own rows and, with a window, the rows past the
-window's reach in the masked kernel, the rows in between (which see every
-key of the block) in the mask-free one.
+launches: each key block's own rows in the masked kernel (with a window that
+is a multiple of 32 rows, at least 512 and shorter than the chunk, paired in
+the same launch with the rows at the window's edge, each wave taking the one
+of the two tiles it sees), and the rows in between (which see every key of
+the block) in the mask-free one.
 Every gradient is compared element by element with the float64 oracle, on
 shapes that take the banded path and on one that just misses it (a window
 that is not a multiple of 32 rows), and repeated runs must agree bit for
@@ -31,10 +32,12 @@ def _need_gpu(dfa_lib):
 
 @pytest.mark.parametrize("b,l,start,hq,hkv,dh,win,launches", [
     (2, 2048, 0, 16, 16, 128, 0, 2),       # own rows masked, the rest mask-free
-    (2, 2048, 0, 16, 16, 128, 512, 3),     # three bands, the smallest window that bands
-    (2, 2048, 4096, 16, 16, 64, 800, 3),   # head_dim 64, non-zero chunk start, 25-tile window
+    (2, 2048, 0, 16, 16, 128, 512, 2),     # paired bands, the smallest window that bands
+    (2, 2048, 4096, 16, 16, 64, 800, 2),   # head_dim 64, non-zero chunk start, 25-tile window
     (16, 2048, 0, 8, 2, 64, 0, 2),         # four query heads per key/value head
-    (2, 2560, 0, 16, 16, 128, 1024, 3),    # late blocks' window band cut by the chunk's end
+    (2, 2560, 0, 16, 16, 128, 1024, 2),    # late blocks' window-edge tiles cut by the chunk's end
+    (8, 1024, 0, 32, 8, 128, 544, 2),      # window-edge tiles of a 17-tile window, GQA 4
+    (2, 2048, 0, 16, 16, 128, 2048, 2),    # window as long as the chunk: own rows alone
     (2, 2048, 0, 16, 16, 128, 500, 1),     # not a multiple of 32 rows: one masked launch
 ])
 def test_banded_diagonal_pair_backward(b, l, start, hq, hkv, dh, win, launches):

@@ -1,14 +1,16 @@
 """Seeded random chunk pairs of medium size (up to 2100 x 2100 tokens), drawn
 so that the bf16 kernels take every launch path: fully visible pairs (the
-mask-free kernels), masked pairs, diagonal pairs whose dK/dV runs as two or
-three row bands, and pairs whose dK/dV rows are split over workgroups with a
-fixed-order reduction.  Each pair is diagonal, fully visible, a band (query
-chunk starting inside the key chunk), random offsets or non-causal; lengths
-are ragged or whole 256-token blocks; windows of 1 to 5000 tokens; 1 to 64
-query heads, grouping 1 to 8, batch 1 to 3, head_dim 64 or 128.  Forward (O,
-LSE) and backward (dQ, dK, dV from the oracle's O and LSE) against the
-float64 oracle.  Which path a case takes comes from the library's own
-host-side plan (launch count and workspace size), checked on the CPU."""
+mask-free kernels), masked pairs, diagonal pairs whose dK/dV runs as two row
+bands (with a window shorter than the chunk, the first pairs each key block's
+own rows with its window-edge rows), and pairs whose dK/dV rows are split
+over workgroups with a fixed-order reduction.  Each pair is diagonal, fully
+visible, a band (query chunk starting inside the key chunk), random offsets
+or non-causal; lengths are ragged or whole 256-token blocks; windows of 1 to
+5000 tokens; 1 to 64 query heads, grouping 1 to 8, batch 1 to 3, head_dim 64
+or 128.  Forward (O, LSE) and backward (dQ, dK, dV from the oracle's O and
+LSE) against the float64 oracle.  Which path a case takes comes from the
+library's own host-side plan (launch count and workspace size), checked on
+the CPU."""
 
 from collections import Counter
 
@@ -73,9 +75,10 @@ def _path(case):
     d = _desc(case)
     if D.dfa_attn_workspace_size(d, D.DFA_OP_BWD) > 0:
         return "row split"
-    n = D.dfa_test_bwd_launches(d, 1)
-    if n > 1:
-        return f"{n} row bands"
+    if D.dfa_test_bwd_launches(d, 1) > 1:
+        # with a window shorter than the chunk the own rows and the rows at the
+        # window's edge share one paired launch
+        return "paired row bands" if 0 < win < lq else "row bands"
     sees_all = (not causal or q0 >= k0 + lk - 1) and (win == 0 or q0 + lq - 1 - k0 < win)
     return "mask-free" if sees_all and lk % 256 == 0 else "masked"
 
@@ -83,7 +86,7 @@ def _path(case):
 def test_cases_take_every_launch_path(dfa_lib):
     """CPU: the drawn cases reach every path (so the GPU test below covers them)."""
     paths = Counter(_path(c) for c in CASES)
-    assert set(paths) == {"row split", "2 row bands", "3 row bands", "mask-free", "masked"}, paths
+    assert set(paths) == {"row split", "row bands", "paired row bands", "mask-free", "masked"}, paths
 
 
 @pytest.mark.gpu
