@@ -299,7 +299,7 @@ dfa_status dfa_test_bwd_part(const dfa_attn_desc* desc, const void* q,
 
 /* Kernel launches that dfa_test_bwd_part(desc, ..., part, ...) makes for
  * its kernel (part 1: the dK/dV kernel, whose diagonal pairs of whole
- * 256-key blocks run as two or three row-band launches; part 2: the dQ
+ * 256-key blocks run as two row-band launches; part 2: the dQ
  * kernel, one launch), written to *launches; 0 for a pair without query
  * rows or keys.  Host arithmetic only (no HIP call): a per-launch time is
  * a call's time divided by this count. */

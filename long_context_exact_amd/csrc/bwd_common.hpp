@@ -83,7 +83,7 @@ BwdArgs bwd_args_of(const dfa_attn_desc& d);
 int64_t dkdv_split_bytes_per_slice(const dfa_attn_desc& d);
 int64_t dkdv_workspace_bytes(const dfa_attn_desc& d);
 // Launches of the dK/dV kernel for a descriptor (row bands make a diagonal
-// pair's dK/dV two or three launches; 0 for an empty pair).  Host only.
+// pair's dK/dV two launches; 0 for an empty pair).  Host only.
 int dkdv_launches(const dfa_attn_desc& d);
 
 // Launchers of the two kernels (head_dim 64 or 128, bf16 operands).

@@ -325,7 +325,8 @@ def test_windowed_worker_share_forward_backward():
     _check_grad_identities(w, host, res, [a], kvs)
 
     # every key's dK / dV of the two window chunks (the diagonal pair's dK/dV
-    # in three row bands), from 64 sampled rows on both sides of the window's
+    # in two row-band launches, the first pairing each key block's own rows
+    # with its window-edge rows), from 64 sampled rows on both sides of the window's
     # reach
     def keys(g):
         kp = np.concatenate([host[1][j][:, :, g:g + 1] for j in kvs], 1).astype(np.float64)
