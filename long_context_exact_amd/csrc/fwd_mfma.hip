@@ -103,14 +103,6 @@ void fwd_bf16_kernel(FwdArgs a) {
   const uint16_t* vtb = a.vt + (b * a.hkv + g) * D * a.vt_ld;  // this head's V^T rows
   const int64_t row = w_lo + l32;  // this lane's query row (local index)
 
-  bf16x8 qf[D / 16];
-  {
-    const uint16_t* qp = a.q + (b * a.len_q + row) * q_rs + int64_t(h) * D;
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st)
-      qf[st] = row < a.len_q ? ld_bf16x8(qp + 16 * st + 8 * hi) : bf16x8{};
-  }
-
   int kt_end = a.n_ktiles;
   if (a.causal) {
     const int64_t lim = a.q_start + (q_hi - 1) - a.kv_start;
@@ -121,6 +113,17 @@ void fwd_bf16_kernel(FwdArgs a) {
   {
     const int64_t lo = a.q_start + q_lo - a.win + 1 - a.kv_start;  // lowest visible key
     if (lo > 0) kt_begin = lo >= a.len_kv ? a.n_ktiles : int(lo / BN);
+  }
+
+  // Q of this lane's row as the B operand of S^T, in VGPRs for the whole
+  // loop; not loaded by a workgroup whose rows see no key tile (it only
+  // writes O = 0, LSE = -inf)
+  bf16x8 qf[D / 16];
+  if (FULL || kt_begin < kt_end) {
+    const uint16_t* qp = a.q + (b * a.len_q + row) * q_rs + int64_t(h) * D;
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st)
+      qf[st] = row < a.len_q ? ld_bf16x8(qp + 16 * st + 8 * hi) : bf16x8{};
   }
 
   f32x16 oacc[D / 32];
