@@ -40,7 +40,6 @@ dfa_status check_desc(const char* fn, const dfa_attn_desc* d) {
   if (d->head_dim != 64 && d->head_dim != 128)
     return fail(DFA_ERR_UNSUPPORTED,
                 f + ": head_dim " + std::to_string(d->head_dim) + " unsupported (64 or 128)");
-  // grid extents: query tiles x head groups must fit a 32-bit grid
   // Kernels stage tiles of at most 256 rows through 32-bit byte offsets from
   // a tile base: 256 rows of heads_q * head_dim elements of up to 4 bytes
   // must stay below 2^31 bytes.
@@ -49,6 +48,7 @@ dfa_status check_desc(const char* fn, const dfa_attn_desc* d) {
                 f + ": heads_q * head_dim must be below 2^21 (32-bit tile offsets)");
   if (d->len_q > (int64_t(1) << 40) || d->len_kv > (int64_t(1) << 40))
     return fail(DFA_ERR_INVALID, f + ": chunk length too large");
+  // grid extents: row tiles x heads (with a margin) must fit a 32-bit grid
   if (cdiv(d->len_q, 4) * d->heads_q > INT32_MAX || cdiv(d->len_kv, 4) * d->heads_kv > INT32_MAX)
     return fail(DFA_ERR_INVALID, f + ": problem exceeds the launch grid");
   return DFA_OK;
