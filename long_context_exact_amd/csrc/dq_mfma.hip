@@ -53,7 +53,7 @@ void dq_bf16_kernel(BwdArgs a) {
 
   bf16x8 qf[D / 16], df[D / 16];
   float lse2 = INFINITY, dl = 0.f;
-  {
+  auto load_rows = [&]() {
     const int64_t off = (b * a.len_q + row) * q_rs + int64_t(h) * D;
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
@@ -65,7 +65,11 @@ void dq_bf16_kernel(BwdArgs a) {
       lse2 = lse2_of(a.lse[li]);
       dl = a.delta[li];
     }
-  }
+  };
+  // Every tile of a fully visible pair has keys for every row; elsewhere a
+  // workgroup whose rows see no key (nothing to add to dq) leaves before
+  // loading them.
+  if constexpr (FULL) load_rows();
 
   int kt_end = a.n_ktiles;
   if (a.causal) {
@@ -78,6 +82,7 @@ void dq_bf16_kernel(BwdArgs a) {
     if (lo > 0) kt_begin = lo >= a.len_kv ? a.n_ktiles : int(lo / BN);
   }
   if (kt_begin >= kt_end) return;  // uniform: no key visible to any row here
+  if constexpr (!FULL) load_rows();
 
   f32x16 acc[D / 32];
 #pragma unroll
