@@ -35,7 +35,8 @@ struct DkvCfg {
   static_assert(LDS_BYTES <= 160 * 1024 && LDS_BYTES_PAIR <= 160 * 1024, "fits gfx950 LDS");
 };
 
-// TM: tile-major step order (see tile_of below), for pairs without a window.
+// TM: tile-major step order (see tile_of below), for pairs without a window
+// and, with ROT, for the mask-free band of a windowed diagonal pair.
 // PAIR: the two masked row bands of a windowed diagonal pair in one launch.
 // Of a key block's own row tiles (0 .. BK/BQ - 1 from its first row, where
 // the causal edge crosses it) wave w sees only tiles t >= w, and of the
@@ -44,11 +45,12 @@ struct DkvCfg {
 // one of the two it sees (own if p - 1 >= w, else edge): BK/BQ + 1 steps per
 // head in which every wave works, against 2 * BK/BQ steps run as two bands
 // in which half the waves idle on average.
-template <int D, int NW, bool FULL, bool TM, bool PAIR = false>
+template <int D, int NW, bool FULL, bool TM, bool PAIR = false, bool ROT = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DFA_BWD_OCC, DFA_BWD_OCC)))
 void dkdv_bf16_kernel(BwdArgs a) {
   using C = DkvCfg<D, NW>;
   static_assert(!PAIR || (!FULL && !TM), "paired bands run the masked, head-major kernel");
+  static_assert(!ROT || TM, "the rotated order is a tile-major order");
   extern __shared__ __align__(16) uint16_t smem_generic[];
   lds_u16* smem = lds_base(smem_generic);
   lds_u16* Vs = smem;
@@ -85,9 +87,20 @@ void dkdv_bf16_kernel(BwdArgs a) {
   // side by side read the same Q / dO tile at the same time (until each
   // reaches its own first row) and share it in L2 (a diagonal pair's HBM
   // reads drop several-fold).  With a window the row ranges slide with the
-  // key block: heads outermost, tiles ascending, keeps neighbouring blocks a
-  // few steps apart in the same head's rows instead.
-  auto tile_of = [&](int it) { return TM ? qt0 + nq - 1 - it / a.group : qt0 + it % nq; };
+  // key block, by BK/BQ tiles from one block to the next; in the mask-free
+  // band every block's range is equally long, and ROT runs it tile-major in
+  // rotated order, tile t at tile step t (mod nq), so that the blocks running
+  // side by side again reach each tile they share at the same step.  The
+  // masked windowed launches run heads outermost, tiles ascending, which keeps
+  // neighbouring blocks a few steps apart in the same head's rows.
+  const int rot = ROT ? (nq - qt0 % nq) % nq : 0;  // qt0 + rot = 0 (mod nq)
+  auto tile_of = [&](int it) {
+    if constexpr (ROT) {
+      const int t = it / a.group + rot;
+      return qt0 + (t >= nq ? t - nq : t);
+    }
+    return TM ? qt0 + nq - 1 - it / a.group : qt0 + it % nq;
+  };
   auto head_of = [&](int it) {
     return g * a.group + (TM ? it % a.group : it / (PAIR ? C::NPAIR : nq));
   };
@@ -542,7 +555,7 @@ dfa_status launch_dkdv(const dfa_attn_desc& d, BwdArgs a, hipStream_t s) {
     band.band_lo = p.own;
     band.band_hi = p.wt;
     return tm ? go(dkdv_bf16_kernel<D, kDkvNW, true, true>, band)
-              : go(dkdv_bf16_kernel<D, kDkvNW, true, false>, band);
+              : go(dkdv_bf16_kernel<D, kDkvNW, true, true, false, true>, band);
   }
   return rsplit_reduce<D>(d, a, s,
                           tm ? go(dkdv_bf16_kernel<D, kDkvNW, false, true>, a)
