@@ -35,6 +35,7 @@ struct DkvCfg {
   static_assert(LDS_BYTES <= 160 * 1024 && LDS_BYTES_PAIR <= 160 * 1024, "fits gfx950 LDS");
 };
 
+// FULL: every row the launch runs sees every key of the block (no mask code).
 // TM: tile-major step order (see tile_of below), for pairs without a window
 // and, with ROT, for the mask-free band of a windowed diagonal pair.
 // PAIR: the two masked row bands of a windowed diagonal pair in one launch.
