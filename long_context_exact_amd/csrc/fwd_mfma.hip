@@ -196,19 +196,25 @@ void fwd_bf16_kernel(FwdArgs a) {
     m = m_new;
   };
   // O^T += V^T P^T for one sub-block.
-  auto pv = [&](const lds_u16* Vs, int kb, const f32x16& p) {
+  // V^T fragments of one sub-block, read ahead of its softmax: lane (d, hi)
+  // takes keys kb*32 + 16j + 4hi + {0..3, 8..11}, positions 8hi..8hi+7 of the
+  // 16-key group in V^T's permuted order.
+  using VFrags = bf16x8[2 * (D / 32)];
+  auto load_v = [&](const lds_u16* Vs, int kb, VFrags& vf) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+        vf[j * (D / 32) + db] = tile_row8<BN>(Vs, 32 * db + l32, 4 * kb + 2 * j + hi);
+  };
+  auto pv = [&](const VFrags& vf, const f32x16& p) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       bf16x8 pb;
 #pragma unroll
       for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(p[8 * j + e]);
-      // lane (d, hi) takes keys kb*32 + 16j + 4hi + {0..3, 8..11}: positions
-      // 8hi..8hi+7 of the 16-key group in V^T's permuted order
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const bf16x8 va = tile_row8<BN>(Vs, 32 * db + l32, 4 * kb + 2 * j + hi);
-        oacc[db] = mfma32(va, pb, oacc[db]);
-      }
+      for (int db = 0; db < D / 32; ++db) oacc[db] = mfma32(vf[j * (D / 32) + db], pb, oacc[db]);
     }
   };
 
@@ -259,14 +265,18 @@ void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll  // unrolled: s_cur / s_nxt rename instead of being copied
       for (int kb = 0; kb < C::NSB - 1; ++kb) {
         f32x16 s_nxt = qk(Ks, kb + 1);  // independent of the softmax below
+        VFrags vf;
+        load_v(Vs, kb, vf);
         mask(s_cur, kb);
         softmax(s_cur);
-        pv(Vs, kb, s_cur);
+        pv(vf, s_cur);
         s_cur = s_nxt;
       }
+      VFrags vf;
+      load_v(Vs, C::NSB - 1, vf);
       mask(s_cur, C::NSB - 1);
       softmax(s_cur);
-      pv(Vs, C::NSB - 1, s_cur);
+      pv(vf, s_cur);
     }
     wait_vmem();  // the next tile's segments this wave staged have landed
     __syncthreads();
