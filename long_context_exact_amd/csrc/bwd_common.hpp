@@ -25,8 +25,8 @@ struct BwdArgs {
   float scale;
   int64_t win;  // sliding window in tokens; a huge value when there is none
   // dK/dV row split: each key block's steps are cut into rsplit slices run
-  // by separate workgroups (blockIdx.z), which store their partial dK, dV to
-  // ws ([2][rsplit][B][len_kv][Hkv][d] float32) for a fixed-order reduction;
+  // by separate workgroups, which store their partial dK, dV to ws
+  // ([2][rsplit][B][len_kv][Hkv][d] float32) for a fixed-order reduction;
   // rsplit = 1 adds straight into dk, dv.
   int32_t rsplit;
   float* ws;
@@ -38,6 +38,10 @@ struct BwdArgs {
   // window-edge rows start pair_wt row tiles past each key block's first row
   // (0 for every other launch).
   int32_t pair_wt;
+  // Work order: dQ takes row tiles first to last (rows_up) instead of last to
+  // first, dK/dV key blocks last to first (keys_down) instead of first to
+  // last, when that puts the longest workgroups first.
+  int32_t rows_up, keys_down;
 };
 
 // The query-row steps of the dK/dV workgroup owning keys [k_lo, k_lo + bk):

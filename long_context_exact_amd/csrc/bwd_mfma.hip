@@ -54,6 +54,8 @@ BwdArgs bwd_args_of(const dfa_attn_desc& d) {
   a.band_lo = 0;  // and may run a pair as row bands
   a.band_hi = INT32_MAX;
   a.pair_wt = 0;
+  a.rows_up = 0;
+  a.keys_down = 0;
   return a;
 }
 

@@ -61,8 +61,17 @@ void dkdv_bf16_kernel(BwdArgs a) {
   const int lane = tid & 63;
   const int l32 = lane & 31, hi = lane >> 5;
   const int half16 = (lane >> 4) & 1;
-  const int kt = blockIdx.x / a.hkv;
-  const int g = blockIdx.x % a.hkv;
+  // Workgroups in dispatch order (x, then z over the row slices) enumerate
+  // (key block, row slice, key-value head) with heads fastest: workgroup i
+  // runs on XCD i mod 8, so with 8 key-value heads each XCD serves one head's
+  // K, V and rows.  The slices of a key block run side by side, and the key
+  // blocks go first to last, or last to first when the later keys see more
+  // rows (keys_down), so that the longest workgroups start first.
+  const int wg = int(blockIdx.z * gridDim.x + blockIdx.x);
+  const int g = wg % a.hkv;
+  const int slice = wg / a.hkv % a.rsplit;
+  const int rank = wg / (a.hkv * a.rsplit);
+  const int kt = a.keys_down ? int(gridDim.x) / a.hkv - 1 - rank : rank;
   const int64_t b = blockIdx.y;
   const int64_t k_lo = int64_t(kt) * C::BK;
   const int64_t wk_lo = k_lo + wave * 32;
@@ -74,12 +83,12 @@ void dkdv_bf16_kernel(BwdArgs a) {
   const int64_t kv_rs = int64_t(a.hkv) * D;
 
   // This workgroup's steps: its key block's query-row steps, or with a row
-  // split the blockIdx.z-th slice of them (uniform over the workgroup).
+  // split the slice-th slice of them (uniform over the workgroup).
   const DkvSpan sp = dkdv_span(a, k_lo, C::BK, C::BQ);
   const int qt0 = sp.qt0, nq = sp.nq;
   const int n_steps = PAIR ? (sp.steps > 0 ? C::NPAIR * a.group : 0) : sp.steps;
   const int per = int(cdiv(n_steps, a.rsplit));
-  const int it0 = int(blockIdx.z) * per;
+  const int it0 = slice * per;
   const int it1 = min(n_steps, it0 + per);
   if (it0 >= it1) return;  // the reduction skips slices without steps
   // Step it covers query tile tile_of(it) of head head_of(it).  Without a
@@ -384,7 +393,7 @@ void dkdv_bf16_kernel(BwdArgs a) {
   if (!wave_active || key >= a.len_kv) return;
   if (a.rsplit > 1) {  // store this slice's partial for the reduction
     const int64_t n = int64_t(a.rsplit) * gridDim.y * a.len_kv * kv_rs;
-    float* wk = a.ws + ((int64_t(blockIdx.z) * gridDim.y + b) * a.len_kv + key) * kv_rs +
+    float* wk = a.ws + ((int64_t(slice) * gridDim.y + b) * a.len_kv + key) * kv_rs +
                 int64_t(g) * D;
     float* wv = wk + n;
 #pragma unroll
@@ -528,6 +537,8 @@ dfa_status launch_dkdv(const dfa_attn_desc& d, BwdArgs a, hipStream_t s) {
   // checked before this call).
   a.rsplit = p.rsplit;
   a.ws = a.rsplit > 1 ? static_cast<float*>(d.workspace) : nullptr;
+  a.keys_down = dkdv_span(a, (nkb - 1) * C::BK, C::BK, C::BQ).steps >
+                dkdv_span(a, 0, C::BK, C::BQ).steps;
   dim3 grid(unsigned(nkb) * unsigned(d.heads_kv), unsigned(d.batch), unsigned(a.rsplit));
   auto go = [&](auto kern, const BwdArgs& args, int lds_bytes = C::LDS_BYTES) {
     const dfa_status st = allow_lds(kern, lds_bytes, "dkdv_bf16_kernel");

@@ -41,7 +41,7 @@ void dq_bf16_kernel(BwdArgs a) {
   const int l32 = lane & 31, hi = lane >> 5;
   const int half16 = (lane >> 4) & 1;
   const int bid = blockIdx.x;
-  const int qt = a.n_tiles - 1 - bid / a.n_hgroups;
+  const int qt = a.rows_up ? bid / a.n_hgroups : a.n_tiles - 1 - bid / a.n_hgroups;
   const int hg = bid % a.n_hgroups;
   const int64_t b = blockIdx.y;
   const int h = hg * HPW + wave % HPW;
@@ -249,6 +249,7 @@ dfa_status launch_dq(const dfa_attn_desc& d, BwdArgs a, hipStream_t s) {
   a.n_tiles = int(cdiv(d.len_q, C::BM));
   a.n_hgroups = d.heads_q / HPW;
   a.n_ktiles = int(cdiv(d.len_kv, kDqBN));
+  a.rows_up = rows_heaviest_first(d);
   dim3 grid(unsigned(a.n_tiles) * unsigned(a.n_hgroups), unsigned(d.batch));
   auto go = [&](auto kern) {
     const dfa_status st = allow_lds(kern, C::LDS_BYTES, "dq_bf16_kernel");

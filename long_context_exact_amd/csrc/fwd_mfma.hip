@@ -11,9 +11,10 @@
 //   workgroup = NW waves; wave w owns 32 query rows of query head
 //   hg*HPW + w%HPW (HPW heads of one grouped-query group share each K/V
 //   tile); the workgroup's query tile is BM = 32 * NW/HPW rows.
-//   Grid x enumerates (query tile, head group) with the heaviest (latest)
-//   query tiles first and head groups fastest, so that with >= 8 head
-//   groups the workgroups of one key/value head stay on one XCD's L2.
+//   Grid x enumerates (query tile, head group) with the heaviest query
+//   tiles first (the latest, or with a window whose edge leaves the key
+//   chunk behind, the earliest) and head groups fastest, so that with >= 8
+//   head groups the workgroups of one key/value head stay on one XCD's L2.
 // Per key tile of BN keys, staged straight from HBM into LDS
 // (global_load_lds, row-major, swizzled, double-buffered):
 //   S^T = K Q^T        (A = K rows from LDS, B = Q fragments in VGPRs),
@@ -51,6 +52,7 @@ struct FwdArgs {
   int32_t n_qtiles, n_ktiles, n_hgroups;
   float c;  // scale * log2(e), > 0
   int64_t win;  // sliding window in tokens; a huge value when there is none
+  int32_t rows_up;  // row tiles first to last (the first rows see the most keys)
 };
 
 template <int D, int NW, int HPW, int BN>
@@ -86,7 +88,7 @@ void fwd_bf16_kernel(FwdArgs a) {
   const int l32 = lane & 31, hi = lane >> 5;
   const int half16 = (lane >> 4) & 1;  // which 16 columns of a 32-wide block
   const int bid = blockIdx.x;
-  const int qt = a.n_qtiles - 1 - bid / a.n_hgroups;
+  const int qt = a.rows_up ? bid / a.n_hgroups : a.n_qtiles - 1 - bid / a.n_hgroups;
   const int hg = bid % a.n_hgroups;
   const int64_t b = blockIdx.y;
   const int h = hg * HPW + wave % HPW;
@@ -393,6 +395,7 @@ dfa_status launch_fwd(const dfa_attn_desc& d, const void* q, const void* k, cons
   // every visible key the weight exp2(0) = 1 in fp32.
   a.c = std::max(d.scale * kLog2e, FLT_MIN);
   a.win = d.window > 0 ? d.window : kNoWindow;
+  a.rows_up = rows_heaviest_first(d);
   // V^T into the caller's workspace (stream-ordered before the forward kernel;
   // its size was checked against fwd_workspace_bytes before this call)
   a.vt_ld = cdiv(d.len_kv, kBN) * kBN;

@@ -52,6 +52,23 @@ inline bool pair_is_full(const dfa_attn_desc& d, int64_t tile) {
   return all_visible && in_window && d.len_kv % tile == 0;
 }
 
+// Whether the pair's first query row sees more keys than its last one (a
+// sliding window whose edge leaves the key chunk behind the later rows): the
+// forward and dQ then hand out row tiles first to last instead of last to
+// first, so that in either case the longest workgroups start first and the
+// short ones fill the end of the launch.
+inline bool rows_heaviest_first(const dfa_attn_desc& d) {
+  if (d.len_q <= 0 || d.len_kv <= 0) return false;
+  auto seen = [&](int64_t r) {  // keys visible to local query row r
+    const int64_t q = d.q_start + r;
+    int64_t hi = d.kv_start + d.len_kv - 1, lo = d.kv_start;
+    if (d.causal && q < hi) hi = q;
+    if (d.window > 0 && q - d.window + 1 > lo) lo = q - d.window + 1;
+    return hi >= lo ? hi - lo + 1 : int64_t(0);
+  };
+  return seen(0) > seen(d.len_q - 1);
+}
+
 // Device workspace (bytes) the forward / backward of a descriptor needs:
 // host arithmetic only (no HIP call), so the size query works anywhere.
 int64_t fwd_workspace_bytes(const dfa_attn_desc& d);
