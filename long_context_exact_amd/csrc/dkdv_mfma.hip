@@ -103,21 +103,27 @@ void dkdv_bf16_kernel(BwdArgs a) {
   // side by side again reach each tile they share at the same step.  The
   // masked windowed launches run heads outermost, tiles ascending, which keeps
   // neighbouring blocks a few steps apart in the same head's rows.
+  // A step's position is it = major * M + minor: tile step and head (TM),
+  // head and tile (head-major), head and paired step (PAIR).  It is divided
+  // out once and then advanced step by step (scalar adds, no division).
   const int rot = ROT ? (nq - qt0 % nq) % nq : 0;  // qt0 + rot = 0 (mod nq)
-  auto tile_of = [&](int it) {
+  const int M = TM ? a.group : (PAIR ? C::NPAIR : nq);
+  struct Pos {
+    int major, minor;
+  };
+  auto advance = [&](Pos p) { return p.minor + 1 == M ? Pos{p.major + 1, 0} : Pos{p.major, p.minor + 1}; };
+  auto tile_of = [&](Pos p) {
     if constexpr (ROT) {
-      const int t = it / a.group + rot;
+      const int t = p.major + rot;
       return qt0 + (t >= nq ? t - nq : t);
     }
-    return TM ? qt0 + nq - 1 - it / a.group : qt0 + it % nq;
+    return TM ? qt0 + nq - 1 - p.major : qt0 + p.minor;
   };
-  auto head_of = [&](int it) {
-    return g * a.group + (TM ? it % a.group : it / (PAIR ? C::NPAIR : nq));
-  };
-  // PAIR: the own and the edge tile of step it (tile indices from the chunk's
+  auto head_of = [&](Pos p) { return g * a.group + (TM ? p.minor : p.major); };
+  // PAIR: the own and the edge tile of a step (tile indices from the chunk's
   // first row) and whether each holds rows of this key block's span.
-  auto pair_tiles = [&](int it, int& own_t, int& edge_t, bool& own_ok, bool& edge_ok) {
-    const int pp = it % C::NPAIR;
+  auto pair_tiles = [&](Pos p, int& own_t, int& edge_t, bool& own_ok, bool& edge_ok) {
+    const int pp = p.minor;
     own_t = qt0 + pp - 1;
     edge_t = qt0 + a.pair_wt + pp;
     own_ok = pp >= 1 && pp - 1 < nq;
@@ -152,11 +158,11 @@ void dkdv_bf16_kernel(BwdArgs a) {
   auto stage_ptr = [&](int stage) {
     return smem + C::KV_TILE + stage * (PAIR ? 2 * C::STAGE : C::STAGE);
   };
-  auto stage_q_pair = [&](int it, int stage) {
-    const int h = head_of(it);
+  auto stage_q_pair = [&](Pos ps, int stage) {
+    const int h = head_of(ps);
     int own_t, edge_t;
     bool own_ok, edge_ok;
-    pair_tiles(it, own_t, edge_t, own_ok, edge_ok);
+    pair_tiles(ps, own_t, edge_t, own_ok, edge_ok);
     const uint16_t* qb = a.q + b * a.len_q * q_rs + int64_t(h) * D;
     const uint16_t* db_ = a.d_o + b * a.len_q * q_rs + int64_t(h) * D;
     int ln = lane;
@@ -179,13 +185,13 @@ void dkdv_bf16_kernel(BwdArgs a) {
                          last_row);
     }
   };
-  auto stage_q = [&](int it, int stage) {
+  auto stage_q = [&](Pos ps, int stage) {
     if constexpr (PAIR) {
-      stage_q_pair(it, stage);
+      stage_q_pair(ps, stage);
       return;
     }
-    const int h = head_of(it);
-    const int64_t i0 = int64_t(tile_of(it)) * C::BQ;
+    const int h = head_of(ps);
+    const int64_t i0 = int64_t(tile_of(ps)) * C::BQ;
     const uint16_t* qb = a.q + b * a.len_q * q_rs + int64_t(h) * D;
     const uint16_t* db_ = a.d_o + b * a.len_q * q_rs + int64_t(h) * D;
     lds_u16* Qs = stage_ptr(stage);
@@ -197,6 +203,11 @@ void dkdv_bf16_kernel(BwdArgs a) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
     // 2 * Q_SEGS segments (Q then dO) spread over the waves
+    if constexpr (C::Q_SEGS == NW) {  // segment `wave` of each, without a branch on it
+      tile_dma_rows<D>(Qs, wave, ln, qb + i0 * q_rs, uint32_t(q_rs * 2), last_row);
+      tile_dma_rows<D>(dOs, wave, ln, db_ + i0 * q_rs, uint32_t(q_rs * 2), last_row);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 2 * C::Q_SEGS / NW; ++i) {
       const int seg = wave + i * NW;
@@ -217,12 +228,12 @@ void dkdv_bf16_kernel(BwdArgs a) {
   static_assert(C::BQ <= 64, "one lane per row of a step");
   float raw_l = 0.f, raw_d = 0.f;
   bool raw_ok = false;
-  auto load_stats = [&](int it) {
-    const int h = head_of(it);
+  auto load_stats = [&](Pos ps) {
+    const int h = head_of(ps);
     if constexpr (PAIR) {  // lanes 0..31: the own tile's rows, 32..63: the edge tile's
       int own_t, edge_t;
       bool own_ok, edge_ok;
-      pair_tiles(it, own_t, edge_t, own_ok, edge_ok);
+      pair_tiles(ps, own_t, edge_t, own_ok, edge_ok);
       const bool edge = lane >= C::BQ;
       const int64_t row = int64_t(edge ? edge_t : own_t) * C::BQ + (lane & (C::BQ - 1));
       raw_ok = (edge ? edge_ok : own_ok) && row >= 0 && row < a.len_q;
@@ -231,7 +242,7 @@ void dkdv_bf16_kernel(BwdArgs a) {
       raw_d = a.delta[li];
       return;
     }
-    const int64_t row = int64_t(tile_of(it)) * C::BQ + lane;
+    const int64_t row = int64_t(tile_of(ps)) * C::BQ + lane;
     raw_ok = lane < C::BQ && (FULL || row < a.len_q);
     const int64_t li = (b * a.hq + h) * a.len_q + min<int64_t>(row, a.len_q - 1);
     raw_l = a.lse[li];
@@ -257,8 +268,9 @@ void dkdv_bf16_kernel(BwdArgs a) {
     }
   };
 
-  stage_q(it0, 0);
-  if (wave == 0) load_stats(it0);
+  Pos cur{it0 / M, it0 % M};
+  stage_q(cur, 0);
+  if (wave == 0) load_stats(cur);
   wait_vmem();
   if (wave == 0) store_stats(0);
   __syncthreads();
@@ -266,9 +278,10 @@ void dkdv_bf16_kernel(BwdArgs a) {
 #pragma unroll 1
   for (int it = it0; it < it1; ++it) {
     const int stage = (it - it0) & 1;
+    const Pos nxt = advance(cur);
     if (it + 1 < it1) {  // lands while this step computes
-      stage_q(it + 1, stage ^ 1);
-      if (wave == 0) load_stats(it + 1);
+      stage_q(nxt, stage ^ 1);
+      if (wave == 0) load_stats(nxt);
     }
     const lds_u16* Qs = stage_ptr(stage);
     int64_t r0;  // first row of this step's tile (for this wave)
@@ -276,13 +289,13 @@ void dkdv_bf16_kernel(BwdArgs a) {
     if constexpr (PAIR) {
       int own_t, edge_t;
       bool own_ok, edge_ok;
-      pair_tiles(it, own_t, edge_t, own_ok, edge_ok);
-      const bool own = it % C::NPAIR - 1 >= wave;  // this wave's keys are seen by the own tile
+      pair_tiles(cur, own_t, edge_t, own_ok, edge_ok);
+      const bool own = cur.minor - 1 >= wave;  // this wave's keys are seen by the own tile
       if (!own) Qs += C::STAGE;
       r0 = int64_t(own ? own_t : edge_t) * C::BQ;
       if (!(own ? own_ok : edge_ok)) any = false;
     } else {
-      r0 = int64_t(tile_of(it)) * C::BQ;
+      r0 = int64_t(tile_of(cur)) * C::BQ;
     }
     const lds_u16* dOs = Qs + C::Q_TILE;
     const lds_f32* stats = reinterpret_cast<const lds_f32*>(Qs + 2 * C::Q_TILE);
@@ -388,6 +401,7 @@ void dkdv_bf16_kernel(BwdArgs a) {
       if (wave == 0) store_stats(stage ^ 1);
     }
     __syncthreads();
+    cur = nxt;
   }
 
   if (!wave_active || key >= a.len_kv) return;
