@@ -306,6 +306,18 @@ dfa_status dfa_test_bwd_part(const dfa_attn_desc* desc, const void* q,
 dfa_status dfa_test_bwd_launches(const dfa_attn_desc* desc, int32_t part,
                                  int32_t* launches);
 
+/* Order in which the bf16 kernels hand out a pair's work, so that the
+ * longest workgroups start first: *rows_first_to_last = 1 when the forward
+ * and dQ take query-row tiles first to last (the pair's first row sees more
+ * keys than its last, as in a band pair whose sliding window leaves the key
+ * chunk behind the later rows), 0 for last to first; *keys_last_to_first = 1
+ * when dK/dV takes its 256-key blocks last to first (its last block has more
+ * query-row steps than its first), 0 for first to last.  The order changes no
+ * result.  Host arithmetic only (no HIP call); DFA_ERR_INVALID for a bad
+ * descriptor or a null output pointer. */
+dfa_status dfa_test_work_order(const dfa_attn_desc* desc, int32_t* rows_first_to_last,
+                               int32_t* keys_last_to_first);
+
 
 #ifdef __cplusplus
 }

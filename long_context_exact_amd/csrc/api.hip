@@ -232,6 +232,20 @@ extern "C" dfa_status dfa_test_bwd_launches(const dfa_attn_desc* desc, int32_t p
   }
 }
 
+extern "C" dfa_status dfa_test_work_order(const dfa_attn_desc* desc, int32_t* rows_first_to_last,
+                                          int32_t* keys_last_to_first) {
+  try {
+    DFA_TRY(check_desc("dfa_test_work_order", desc));
+    if (rows_first_to_last == nullptr || keys_last_to_first == nullptr)
+      return fail(DFA_ERR_INVALID, "dfa_test_work_order: output pointer is null");
+    *rows_first_to_last = rows_heaviest_first(*desc) ? 1 : 0;
+    *keys_last_to_first = dkdv_keys_down(*desc) ? 1 : 0;
+    return DFA_OK;
+  } catch (...) {
+    return fail(DFA_ERR_INVALID, "dfa_test_work_order: internal error");
+  }
+}
+
 extern "C" dfa_status dfa_attn_workspace_size(const dfa_attn_desc* desc, int32_t op,
                                               int64_t* bytes) {
   try {

@@ -89,6 +89,9 @@ int64_t dkdv_workspace_bytes(const dfa_attn_desc& d);
 // Launches of the dK/dV kernel for a descriptor (row bands make a diagonal
 // pair's dK/dV two launches; 0 for an empty pair).  Host only.
 int dkdv_launches(const dfa_attn_desc& d);
+// Whether the dK/dV kernel takes the descriptor's key blocks last to first
+// (its last block has more row steps than its first).  Host only.
+bool dkdv_keys_down(const dfa_attn_desc& d);
 
 // Launchers of the two kernels (head_dim 64 or 128, bf16 operands).
 dfa_status launch_dkdv_bf16(const dfa_attn_desc& d, const BwdArgs& a, hipStream_t s);

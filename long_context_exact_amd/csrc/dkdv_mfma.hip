@@ -551,8 +551,7 @@ dfa_status launch_dkdv(const dfa_attn_desc& d, BwdArgs a, hipStream_t s) {
   // checked before this call).
   a.rsplit = p.rsplit;
   a.ws = a.rsplit > 1 ? static_cast<float*>(d.workspace) : nullptr;
-  a.keys_down = dkdv_span(a, (nkb - 1) * C::BK, C::BK, C::BQ).steps >
-                dkdv_span(a, 0, C::BK, C::BQ).steps;
+  a.keys_down = dkdv_keys_down(d);
   dim3 grid(unsigned(nkb) * unsigned(d.heads_kv), unsigned(d.batch), unsigned(a.rsplit));
   auto go = [&](auto kern, const BwdArgs& args, int lds_bytes = C::LDS_BYTES) {
     const dfa_status st = allow_lds(kern, lds_bytes, "dkdv_bf16_kernel");
@@ -605,6 +604,16 @@ dfa_status rsplit_reduce(const dfa_attn_desc& d, const BwdArgs& a, hipStream_t s
 dfa_status launch_dkdv_bf16(const dfa_attn_desc& d, const BwdArgs& a, hipStream_t s) {
   if (d.head_dim == 128) return launch_dkdv<128>(d, a, s);
   return launch_dkdv<64>(d, a, s);
+}
+
+bool dkdv_keys_down(const dfa_attn_desc& d) {
+  using C = DkvCfg<128, kDkvNW>;
+  static_assert(C::BK == DkvCfg<64, kDkvNW>::BK && C::BQ == DkvCfg<64, kDkvNW>::BQ,
+                "key blocks and row steps do not depend on head_dim");
+  if (d.batch == 0 || d.len_q == 0 || d.len_kv == 0) return false;
+  const BwdArgs a = bwd_args_of(d);
+  const int64_t nkb = cdiv(d.len_kv, C::BK);
+  return dkdv_span(a, (nkb - 1) * C::BK, C::BK, C::BQ).steps > dkdv_span(a, 0, C::BK, C::BQ).steps;
 }
 
 int dkdv_launches(const dfa_attn_desc& d) {

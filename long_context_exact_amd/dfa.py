@@ -32,7 +32,7 @@ EXPORTED = (
     "dfa_attn_fwd_partial", "dfa_lse_merge", "dfa_attn_bwd", "dfa_attn_workspace_size",
     "dfa_chunk_transfer", "dfa_attn_fwd_partial_noalloc",
     "dfa_last_error", "dfa_version", "dfa_test_tile_shape", "dfa_test_fwd_tile_visits",
-    "dfa_test_bwd_part", "dfa_test_bwd_launches",
+    "dfa_test_bwd_part", "dfa_test_bwd_launches", "dfa_test_work_order",
 )
 
 
@@ -96,6 +96,8 @@ def lib() -> ctypes.CDLL:
         L.dfa_test_bwd_part.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, P, P, I32,
                                         P]
         L.dfa_test_bwd_launches.argtypes = [ctypes.POINTER(AttnDesc), I32, ctypes.POINTER(I32)]
+        L.dfa_test_work_order.argtypes = [ctypes.POINTER(AttnDesc), ctypes.POINTER(I32),
+                                          ctypes.POINTER(I32)]
         L.dfa_attn_workspace_size.argtypes = [ctypes.POINTER(AttnDesc), I32, ctypes.POINTER(I64)]
         L.dfa_chunk_transfer.argtypes = [P, P, I64, P]
         L.dfa_attn_fwd_partial_noalloc.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P]
@@ -103,7 +105,7 @@ def lib() -> ctypes.CDLL:
                      "dfa_attn_fwd_partial", "dfa_lse_merge", "dfa_attn_workspace_size",
                      "dfa_chunk_transfer", "dfa_attn_fwd_partial_noalloc",
                      "dfa_attn_bwd", "dfa_test_tile_shape", "dfa_test_fwd_tile_visits",
-                     "dfa_test_bwd_part", "dfa_test_bwd_launches"):
+                     "dfa_test_bwd_part", "dfa_test_bwd_launches", "dfa_test_work_order"):
             getattr(L, name).restype = I32
         L.dfa_last_error.argtypes = []
         L.dfa_last_error.restype = ctypes.c_char_p
@@ -334,6 +336,13 @@ def dfa_test_bwd_launches(desc: AttnDesc, part: int) -> int:
     n = ctypes.c_int32(-1)
     _check(lib().dfa_test_bwd_launches(ctypes.byref(desc), int(part), ctypes.byref(n)))
     return n.value
+
+
+def dfa_test_work_order(desc: AttnDesc):
+    """(rows first to last, dK/dV key blocks last to first) for the pair (host only)."""
+    r, k = ctypes.c_int32(-1), ctypes.c_int32(-1)
+    _check(lib().dfa_test_work_order(ctypes.byref(desc), ctypes.byref(r), ctypes.byref(k)))
+    return bool(r.value), bool(k.value)
 
 
 def dfa_test_bwd_part(desc: AttnDesc, q, k, v, lse, d_o, delta, dq, dk, dv, part: int,

@@ -383,3 +383,60 @@ def test_chunk_transfer_argument_errors(dfa_lib):
     assert "overlap" in dfa_lib.dfa_last_error()
     assert L.dfa_chunk_transfer(b, a, 4097, None) == D.DFA_ERR_INVALID
     assert L.dfa_chunk_transfer(None, None, 0, None) == D.DFA_OK
+
+
+def _visible_keys(lq, lk, q0, k0, causal, win, r):
+    """Keys of the chunk that local query row r sees (written out plainly)."""
+    q = q0 + r
+    hi = k0 + lk - 1 if not causal else min(k0 + lk - 1, q)
+    lo = k0 if win <= 0 else max(k0, q - win + 1)
+    return max(0, hi - lo + 1)
+
+
+def test_work_order_follows_the_longest_work(dfa_lib):
+    """Host: the forward and dQ take row tiles first to last exactly when the
+    pair's first row sees more keys than its last; dK/dV takes its 256-key
+    blocks last to first exactly when its last block has more query-row steps
+    than its first (32-row steps from the block's first visible row)."""
+    cases = [  # (lq, lk, q0, k0, causal, win)
+        (1024, 1024, 0, 0, True, 0),          # diagonal
+        (1024, 1024, 4096, 0, True, 0),       # fully visible
+        (1024, 1024, 0, 0, False, 0),         # non-causal
+        (1024, 1024, 0, 0, True, 300),        # windowed diagonal
+        (1024, 1024, 1024, 0, True, 512),     # band pair: the window leaves the key chunk
+        (1024, 1024, 1024, 0, True, 2048),    # band pair the window still covers
+        (1000, 700, 900, 0, True, 400),       # ragged band pair
+        (512, 1536, 1024, 0, True, 0),        # rows starting inside the key chunk
+        (0, 256, 0, 0, True, 0), (256, 0, 0, 0, True, 0),
+    ]
+    seen_rows = seen_keys = 0
+    for lq, lk, q0, k0, causal, win in cases:
+        d = D.make_desc(1, 8, 2, 128, lq, lk, q0, k0, causal, window=win)
+        rows_up, keys_down = D.dfa_test_work_order(d)
+        if lq == 0 or lk == 0:
+            assert (rows_up, keys_down) == (False, False)
+            continue
+        want_rows = (_visible_keys(lq, lk, q0, k0, causal, win, 0) >
+                     _visible_keys(lq, lk, q0, k0, causal, win, lq - 1))
+        assert rows_up == want_rows, (lq, lk, q0, k0, causal, win)
+
+        def steps(j_lo):  # row steps of the key block starting at key j_lo
+            first = None
+            last = -1
+            for r in range(lq):
+                q = q0 + r
+                if any((not causal or k0 + j <= q) and (win <= 0 or q - (k0 + j) < win)
+                       for j in range(j_lo, min(j_lo + 256, lk))):
+                    first = r if first is None else first
+                    last = r
+            return 0 if first is None else (last // 32) - (first // 32) + 1
+        last_block = (lk - 1) // 256 * 256
+        assert keys_down == (steps(last_block) > steps(0)), (lq, lk, q0, k0, causal, win)
+        seen_rows += rows_up
+        seen_keys += keys_down
+    assert seen_rows >= 2 and seen_keys >= 2  # both orders are exercised
+    L = dfa_lib.lib()
+    c = ctypes.c_int32(0)
+    d = D.make_desc(1, 8, 2, 128, 256, 256)
+    assert L.dfa_test_work_order(ctypes.byref(d), None, ctypes.byref(c)) == D.DFA_ERR_INVALID
+    assert L.dfa_test_work_order(None, ctypes.byref(c), ctypes.byref(c)) == D.DFA_ERR_INVALID
